@@ -1,0 +1,225 @@
+/*
+ * sdc_oracle.c -- reference (oracle) implementation.  TEST INFRASTRUCTURE ONLY:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg load it.
+ *
+ * Plain single-threaded C.  Every quantity is a uint64_t, so all sums wrap
+ * modulo 2^64 with defined behaviour.  No blocking, splitting, reordering or
+ * vector tricks: each function walks its input once, in order, exactly as the
+ * definition it cites reads.
+ */
+#include "sdc_oracle.h"
+
+#include <stddef.h>
+#include <string.h>
+
+uint32_t oracle_element_size(uint32_t dtype) {
+  switch (dtype) {
+    case ORACLE_F32: return 4;
+    case ORACLE_BF16: return 2;
+    case ORACLE_F16: return 2;
+    default: return 0;
+  }
+}
+
+/* Raw bit pattern of element i, read byte by byte as little-endian and
+ * zero-extended to 64 bits ("Compare by fingerprint": the sums run over the
+ * elements' raw bit patterns; the unsigned reading is stated in the design
+ * notes). */
+static uint64_t load_bits(const unsigned char* base, uint64_t i, uint32_t esize) {
+  const unsigned char* p = base + i * esize;
+  uint64_t x = 0;
+  for (uint32_t b = 0; b < esize; ++b) x |= (uint64_t)p[b] << (8u * b);
+  return x;
+}
+
+/* NaN or +-Inf: the exponent field is all ones (every NaN payload and sign
+ * counts).  Field positions are those of IEEE binary32, bfloat16 and IEEE
+ * binary16. */
+int oracle_is_nonfinite(uint64_t x, uint32_t dtype) {
+  switch (dtype) {
+    case ORACLE_F32: return (x & 0x7F800000ull) == 0x7F800000ull;
+    case ORACLE_BF16: return (x & 0x7F80ull) == 0x7F80ull;
+    case ORACLE_F16: return (x & 0x7C00ull) == 0x7C00ull;
+    default: return 0;
+  }
+}
+
+/* "Compare by fingerprint": S = sum of x_i, W = sum of (i+1)*x_i, both modulo
+ * 2^64 with 1-based positions; a missing tensor keeps its zero row.
+ * AEGIS review, "core method" item 4: X = xor of the x_i.
+ * Nonfinite count: the element-exact form of the NaN/Inf test of "Check 1". */
+int oracle_fingerprint(const void* data, uint64_t numel, uint32_t dtype, oracle_row* out) {
+  if (out == NULL) return ORACLE_EINVAL;
+  uint32_t esize = oracle_element_size(dtype);
+  if (esize == 0) return ORACLE_EDTYPE;
+  uint64_t s = 0, w = 0, x = 0, nf = 0;
+  if (data != NULL) {
+    const unsigned char* base = (const unsigned char*)data;
+    for (uint64_t i = 0; i < numel; ++i) {
+      uint64_t v = load_bits(base, i, esize);
+      s += v;
+      w += (i + 1) * v;
+      x ^= v;
+      nf += (uint64_t)oracle_is_nonfinite(v, dtype);
+    }
+  }
+  out->sum = s;
+  out->wsum = w;
+  out->xorsum = x;
+  out->nonfinite = nf;
+  return ORACLE_OK;
+}
+
+int oracle_fingerprint_list(const void* const* ptrs, const uint64_t* numels,
+                            const uint32_t* dtypes, uint64_t n, oracle_row* rows) {
+  if (n > 0 && (ptrs == NULL || numels == NULL || dtypes == NULL || rows == NULL))
+    return ORACLE_EINVAL;
+  for (uint64_t k = 0; k < n; ++k) {
+    int rc = oracle_fingerprint(ptrs[k], numels[k], dtypes[k], &rows[k]);
+    if (rc != ORACLE_OK) return rc;
+  }
+  return ORACLE_OK;
+}
+
+int oracle_nonfinite_list(const void* const* ptrs, const uint64_t* numels,
+                          const uint32_t* dtypes, uint64_t n, uint64_t* counts,
+                          uint64_t* total) {
+  if (total == NULL) return ORACLE_EINVAL;
+  if (n > 0 && (ptrs == NULL || numels == NULL || dtypes == NULL || counts == NULL))
+    return ORACLE_EINVAL;
+  uint64_t t = 0;
+  for (uint64_t k = 0; k < n; ++k) {
+    uint32_t esize = oracle_element_size(dtypes[k]);
+    if (esize == 0) return ORACLE_EDTYPE;
+    uint64_t c = 0;
+    if (ptrs[k] != NULL) {
+      const unsigned char* base = (const unsigned char*)ptrs[k];
+      for (uint64_t i = 0; i < numels[k]; ++i)
+        c += (uint64_t)oracle_is_nonfinite(load_bits(base, i, esize), dtypes[k]);
+    }
+    counts[k] = c;
+    t += c;
+  }
+  *total = t;
+  return ORACLE_OK;
+}
+
+static int rows_equal(const oracle_row* a, const oracle_row* b, uint32_t mask) {
+  if ((mask & ORACLE_COL_SUM) && a->sum != b->sum) return 0;
+  if ((mask & ORACLE_COL_WSUM) && a->wsum != b->wsum) return 0;
+  if ((mask & ORACLE_COL_XOR) && a->xorsum != b->xorsum) return 0;
+  if ((mask & ORACLE_COL_NONFINITE) && a->nonfinite != b->nonfinite) return 0;
+  return 1;
+}
+
+/* "Check 3: Weight fingerprints, after the optimizer step": a tensor differs
+ * when some replica's row is not equal to replica 0's.  For each differing
+ * tensor the most common row is found; if it is held by no more than half of
+ * the replicas there is no strict majority and no replica is named;
+ * otherwise every replica whose row differs from it is named. */
+int oracle_majority_compare(const oracle_row* table, uint32_t R, uint64_t T, uint32_t col_mask,
+                            oracle_majority* res, uint8_t* suspect, uint8_t* tensor_status) {
+  if (table == NULL || res == NULL || suspect == NULL || R == 0 || T == 0) return ORACLE_EINVAL;
+  if ((col_mask & ORACLE_COL_ALL) == 0 || (col_mask & ~(uint32_t)ORACLE_COL_ALL) != 0)
+    return ORACLE_EINVAL;
+  res->diverged = 0;
+  res->has_majority = 1;
+  res->n_diff = 0;
+  res->first_diff = UINT64_MAX;
+  res->first_no_majority = UINT64_MAX;
+  for (uint32_t r = 0; r < R; ++r) suspect[r] = 0;
+
+  for (uint64_t k = 0; k < T; ++k) {
+    int differs = 0;
+    for (uint32_t r = 1; r < R; ++r)
+      if (!rows_equal(&table[(uint64_t)r * T + k], &table[k], col_mask)) differs = 1;
+    if (tensor_status != NULL) tensor_status[k] = 0;
+    if (!differs) continue;
+
+    res->diverged = 1;
+    res->n_diff += 1;
+    if (res->first_diff == UINT64_MAX) res->first_diff = k;
+
+    /* Most common row: count, for every replica, how many replicas hold the
+     * same row; keep the first replica with the largest count. */
+    uint32_t best = 0, best_count = 0;
+    for (uint32_t r = 0; r < R; ++r) {
+      uint32_t c = 0;
+      for (uint32_t q = 0; q < R; ++q)
+        if (rows_equal(&table[(uint64_t)q * T + k], &table[(uint64_t)r * T + k], col_mask)) c++;
+      if (c > best_count) { best_count = c; best = r; }
+    }
+    if (2ull * best_count <= (uint64_t)R) {
+      res->has_majority = 0;
+      if (res->first_no_majority == UINT64_MAX) res->first_no_majority = k;
+      if (tensor_status != NULL) tensor_status[k] = 2;
+      continue;
+    }
+    if (tensor_status != NULL) tensor_status[k] = 1;
+    for (uint32_t r = 0; r < R; ++r)
+      if (!rows_equal(&table[(uint64_t)r * T + k], &table[(uint64_t)best * T + k], col_mask))
+        suspect[r] = 1;
+  }
+  /* A single tensor without a strict majority means no replica is named. */
+  if (!res->has_majority)
+    for (uint32_t r = 0; r < R; ++r) suspect[r] = 0;
+  return ORACLE_OK;
+}
+
+/* A single flipped bit b at element i (0-based) moves S by +-2^b, W by
+ * +-(i+1)*2^b with the same sign, and X by exactly 2^b.  This inverts that:
+ * it is a consequence of the definitions of "Compare by fingerprint", not a
+ * rule stated on the pages. */
+int oracle_flip_hint(const oracle_row* a, const oracle_row* b, oracle_hint* hint) {
+  if (a == NULL || b == NULL || hint == NULL) return ORACLE_EINVAL;
+  hint->index = UINT64_MAX;
+  hint->bit = -1;
+  hint->dir = 0;
+  uint64_t dx = a->xorsum ^ b->xorsum;
+  if (dx == 0 || (dx & (dx - 1)) != 0) return ORACLE_OK; /* not exactly one bit */
+  int bit = 0;
+  while (((dx >> bit) & 1u) == 0) bit++;
+  uint64_t ds = b->sum - a->sum;
+  uint64_t dw = b->wsum - a->wsum;
+  int dir;
+  if (ds == dx) {
+    dir = 1;
+  } else if (ds == (uint64_t)0 - dx) {
+    dir = -1;
+    dw = (uint64_t)0 - dw;
+  } else {
+    return ORACLE_OK;
+  }
+  /* dw must equal (i+1) * 2^bit for some i >= 0 with (i+1) * 2^bit < 2^63.
+   * Below that bound (met by any tensor of fewer than 2^32 elements of at
+   * most 4 bytes) the inversion is unique; above it the sign is ambiguous. */
+  if ((dw >> 63) != 0) return ORACLE_OK;
+  uint64_t q = dw >> bit;
+  if (q == 0 || (q << bit) != dw) return ORACLE_OK;
+  hint->index = q - 1;
+  hint->bit = bit;
+  hint->dir = dir;
+  return ORACLE_OK;
+}
+
+/* "Check 2: Ring replay": the replay is compared row by row, for exact
+ * equality, with the original. */
+int oracle_fingerprint_diff(const oracle_row* a, const oracle_row* b, uint64_t T,
+                            uint32_t col_mask, uint64_t* n_diff, uint64_t* idx, uint64_t cap,
+                            oracle_hint* hints) {
+  if (n_diff == NULL || (T > 0 && (a == NULL || b == NULL)) || (cap > 0 && idx == NULL))
+    return ORACLE_EINVAL;
+  if ((col_mask & ORACLE_COL_ALL) == 0 || (col_mask & ~(uint32_t)ORACLE_COL_ALL) != 0)
+    return ORACLE_EINVAL;
+  uint64_t n = 0;
+  for (uint64_t k = 0; k < T; ++k) {
+    if (rows_equal(&a[k], &b[k], col_mask)) continue;
+    if (n < cap) {
+      idx[n] = k;
+      if (hints != NULL) oracle_flip_hint(&a[k], &b[k], &hints[n]);
+    }
+    n++;
+  }
+  *n_diff = n;
+  return ORACLE_OK;
+}
