@@ -1,0 +1,223 @@
+/*
+ * sdc.h -- C ABI of libsdc.so, the MI355X (gfx950) integrity scan for
+ * silent-data-corruption checks in data-parallel training.
+ *
+ * What the library computes comes from these pages:
+ *   [BLOG] AWS Machine Learning Blog, "Detecting and recovering from silent
+ *          data corruption on Amazon SageMaker HyperPod":
+ *          "Compare by fingerprint"           -- the two 64-bit sums per tensor;
+ *          "Check 1: NaN/Inf gradients, ..."   -- NaN/Inf detection;
+ *          "Check 2: Ring replay, ..."         -- exact comparison of a replay
+ *                                                 with the original;
+ *          "Check 3: Weight fingerprints, ..." -- strict-majority comparison
+ *                                                 of the replicas' tables.
+ *   [AEGIS] review page of "Safeguarding LLM Training at Scale: Online SDC
+ *          Detection and Insights from 35 Million GPU Hours", section "core
+ *          method" (核心方法) item 4 -- the xorsum fingerprint.
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns an int32_t status (SDC_OK or a negative SDC_ERR_*).
+ *     No C++ exception or abort crosses the ABI.
+ *   - "d_" arguments are device pointers (HIP device memory of the current
+ *     device), "h_" arguments are host pointers.  The caller owns and allocates
+ *     all memory; the library allocates no device memory and keeps no state
+ *     between calls other than a thread-local copy of the last HIP error.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *     Functions documented as asynchronous only enqueue work on that stream;
+ *     their device outputs are valid once the stream reaches that point.
+ *   - All arithmetic is on unsigned 64-bit integers modulo 2^64; floating
+ *     point data are read as raw bit patterns and never converted, so every
+ *     result is exact and independent of launch shape and scheduling.
+ *   - Functions are thread-safe.  Two scans that write the same output rows
+ *     must not run concurrently.
+ */
+#ifndef SDC_H
+#define SDC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDC_ABI_VERSION 1u
+
+typedef void* sdc_stream_t; /* a hipStream_t */
+
+/* Status codes. */
+enum {
+  SDC_OK = 0,
+  SDC_ERR_INVALID = -1,   /* NULL where data is required, zero R/T, bad column mask, ... */
+  SDC_ERR_DTYPE = -2,     /* unknown element type                                        */
+  SDC_ERR_ALIGN = -3,     /* tensor pointer not aligned to its element size              */
+  SDC_ERR_WORKSPACE = -4, /* plan / workspace buffer smaller than required               */
+  SDC_ERR_HIP = -5,       /* a HIP runtime call failed; see sdc_last_hip_error()         */
+  SDC_ERR_PLAN = -6,      /* plan buffer and plan info do not belong together            */
+  SDC_ERR_RANGE = -7      /* a size exceeds what the library supports                   */
+};
+
+/* Element types.  Only the element width (4 or 2 bytes) and the position of
+ * the exponent field (for the NaN/Inf count) depend on the type. */
+enum { SDC_F32 = 0, SDC_BF16 = 1, SDC_F16 = 2 };
+
+/* Column mask bits for comparisons.  [BLOG] "Check 3" compares (sum, wsum);
+ * SDC_COL_SUM | SDC_COL_WSUM reproduces exactly that comparison. */
+enum {
+  SDC_COL_SUM = 1u, SDC_COL_WSUM = 2u, SDC_COL_XOR = 4u, SDC_COL_NONFINITE = 8u,
+  SDC_COL_ALL = 15u
+};
+
+/* One tensor of the list to scan.
+ *   ptr    device pointer to numel contiguous elements (row-major, little-
+ *          endian), aligned to the element size; NULL means a missing tensor
+ *          (its row is all zero, [BLOG] "Compare by fingerprint").
+ *   numel  number of elements (0 gives a zero row); below 2^62.
+ *   dtype  SDC_F32, SDC_BF16 or SDC_F16.
+ *   flags  must be 0. */
+typedef struct {
+  const void* ptr;
+  uint64_t numel;
+  uint32_t dtype;
+  uint32_t flags;
+} sdc_tensor;
+
+/* Fingerprint row of one tensor, x_i = raw bit pattern of element i
+ * zero-extended to 64 bits, i = 0 .. numel-1:
+ *   sum       = sum_i x_i                 mod 2^64   [BLOG] plain sum
+ *   wsum      = sum_i (i+1) * x_i         mod 2^64   [BLOG] position-weighted sum
+ *   xorsum    = xor_i x_i                            [AEGIS] xorsum
+ *   nonfinite = #{i : exponent field of x_i is all ones} (NaN and +-Inf) */
+typedef struct {
+  uint64_t sum;
+  uint64_t wsum;
+  uint64_t xorsum;
+  uint64_t nonfinite;
+} sdc_row;
+
+/* Host-side summary of a plan, filled by sdc_plan_build and passed back to
+ * the scan calls (it carries the launch size, so no device read is needed). */
+typedef struct {
+  uint64_t magic;        /* identifies the plan; checked against the device copy */
+  uint64_t n_tensors;    /* number of descriptors = number of output rows        */
+  uint64_t n_items;      /* work items = workgroups of one scan launch           */
+  uint64_t n_zero;       /* rows cleared before each scan                        */
+  uint64_t total_elems;  /* elements scanned per pass                            */
+  uint64_t total_bytes;  /* bytes scanned per pass (the algorithmic traffic)     */
+  uint64_t plan_bytes;   /* bytes of the device plan                             */
+  uint64_t item_bytes;   /* bytes per work item (the chunk size used)            */
+} sdc_plan_info;
+
+/* Result of sdc_majority_compare ([BLOG] "Check 3"). */
+typedef struct {
+  int32_t diverged;            /* 1 if some tensor's replica rows are not all equal      */
+  int32_t has_majority;        /* 0 if some differing tensor has no strict majority:
+                                  then no replica is named (h_suspect is all zero)       */
+  uint64_t n_diff;             /* number of differing tensors                            */
+  uint64_t first_diff;         /* smallest differing tensor index, UINT64_MAX if none    */
+  uint64_t first_no_majority;  /* smallest tensor without a strict majority, or UINT64_MAX */
+} sdc_majority;
+
+/* Single-bit-flip localisation of a differing row pair (see sdc_fingerprint_diff). */
+typedef struct {
+  uint64_t index; /* element index of the flipped bit, UINT64_MAX if the change is
+                     not one bit flip */
+  int32_t bit;    /* flipped bit (0 = least significant), -1 if none          */
+  int32_t dir;    /* +1: bit is 0 in a and 1 in b; -1: 1 in a, 0 in b; 0: none */
+} sdc_flip_hint;
+
+/* ---- plans: a fixed tensor list scanned many times ------------------------ */
+
+/* Device bytes needed for the plan of h_tensors[0..n).  item_bytes is the work
+ * item size in bytes (a multiple of 16, at most 4 MiB); 0 selects it
+ * automatically from the total size.  Host-only: no HIP call. */
+int32_t sdc_plan_bytes(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
+                       uint64_t* h_bytes);
+
+/* Packs the descriptors of h_tensors[0..n) into a work list and copies it into
+ * d_plan (plan_bytes bytes of device memory owned by the caller).
+ * SYNCHRONOUS: returns after the copy, ordered on stream, has completed.
+ * h_info receives the host summary needed by the scan calls.  The plan stores
+ * the tensors' device pointers: they must stay valid while the plan is used.
+ * Errors: SDC_ERR_INVALID, SDC_ERR_DTYPE, SDC_ERR_ALIGN, SDC_ERR_RANGE,
+ * SDC_ERR_WORKSPACE (plan_bytes too small), SDC_ERR_HIP. */
+int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
+                       void* d_plan, uint64_t plan_bytes, sdc_plan_info* h_info,
+                       sdc_stream_t stream);
+
+/* [BLOG] "Compare by fingerprint", [AEGIS] xorsum: writes d_out[k] = row of
+ * tensor k for k < n_tensors (d_out: n_tensors * 32 bytes of device memory).
+ * ASYNCHRONOUS on stream: one clearing launch (if any row is split over
+ * several work items) and one scan launch.  Errors: SDC_ERR_INVALID,
+ * SDC_ERR_PLAN, SDC_ERR_HIP. */
+int32_t sdc_fingerprint_plan(const void* d_plan, const sdc_plan_info* h_info, sdc_row* d_out,
+                             sdc_stream_t stream);
+
+/* [BLOG] "Check 1": element-exact NaN/Inf count.  d_counts[k] (uint64 per
+ * tensor, may be NULL) and *d_total receive the counts.  ASYNCHRONOUS.
+ * Errors as sdc_fingerprint_plan. */
+int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info, uint64_t* d_counts,
+                      uint64_t* d_total, sdc_stream_t stream);
+
+/* One-shot form of sdc_plan_build + sdc_fingerprint_plan: d_ws is a device
+ * workspace of at least sdc_plan_bytes(h_tensors, n, 0) bytes that holds the
+ * plan.  The plan upload is synchronous; the scan is asynchronous on stream.
+ * The workspace must not be reused before the scan has completed. */
+int32_t sdc_fingerprint(const sdc_tensor* h_tensors, uint64_t n, void* d_ws, uint64_t ws_bytes,
+                        sdc_row* d_out, sdc_stream_t stream);
+
+/* ---- comparisons of fingerprint tables ------------------------------------ */
+
+/* Device workspace bytes for sdc_majority_compare with R replicas, T tensors. */
+int32_t sdc_majority_ws_bytes(uint32_t R, uint64_t T, uint64_t* h_bytes);
+
+/* [BLOG] "Check 3": strict-majority comparison of R replicas' tables.
+ *   d_table  R*T rows, replica-major: row of replica r, tensor k at r*T + k
+ *            (the layout a scan over the replicas' concatenated lists gives).
+ *   col_mask columns compared (SDC_COL_*; nonzero, no other bits).
+ * For each tensor whose R rows are not all equal: if one row value is held by
+ * more than R/2 replicas, every replica whose row differs from it is named;
+ * otherwise the tensor has no majority, and then no replica is named at all.
+ *   h_res      receives the summary; h_suspect[R] receives 1 for a named
+ *              replica, else 0.
+ *   d_tensor_status  optional (NULL allowed), T bytes of device memory:
+ *              0 = all equal, 1 = differs with a strict majority, 2 = no majority.
+ *   d_ws       sdc_majority_ws_bytes(R, T) bytes of device workspace.
+ * SYNCHRONOUS (waits for stream).  R == 1 never diverges.
+ * Errors: SDC_ERR_INVALID (R == 0, T == 0, NULL, bad mask), SDC_ERR_WORKSPACE,
+ * SDC_ERR_HIP. */
+int32_t sdc_majority_compare(const sdc_row* d_table, uint32_t R, uint64_t T, uint32_t col_mask,
+                             void* d_ws, uint64_t ws_bytes, sdc_majority* h_res,
+                             uint8_t* h_suspect, uint8_t* d_tensor_status, sdc_stream_t stream);
+
+/* Device workspace bytes for sdc_fingerprint_diff over T rows reporting up to
+ * idx_cap indices. */
+int32_t sdc_diff_ws_bytes(uint64_t T, uint64_t idx_cap, uint64_t* h_bytes);
+
+/* [BLOG] "Check 2" (replay vs original) and the check after a restore:
+ * indices k < T with d_a[k] != d_b[k] under col_mask.
+ *   h_n_diff  receives the exact number of differing rows.
+ *   h_idx     receives the first min(n_diff, idx_cap) of them, ascending.
+ *   h_hints   (NULL allowed) receives, for each reported index, the single-bit-
+ *             flip localisation: when X_a ^ X_b = 2^b, S_b - S_a = s * 2^b and
+ *             W_b - W_a = s * (i+1) * 2^b with one sign s = +-1 and
+ *             (i+1) * 2^b < 2^63, the change is one flip of bit b of element i.
+ * SYNCHRONOUS.  Errors: SDC_ERR_INVALID, SDC_ERR_WORKSPACE, SDC_ERR_HIP. */
+int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, uint64_t T, uint32_t col_mask,
+                             void* d_ws, uint64_t ws_bytes, uint64_t* h_n_diff, uint64_t* h_idx,
+                             uint64_t idx_cap, sdc_flip_hint* h_hints, sdc_stream_t stream);
+
+/* ---- misc ------------------------------------------------------------------ */
+
+/* Static text for a status code. */
+const char* sdc_status_string(int32_t status);
+
+/* The hipError_t of the last failed HIP call on this thread (0 if none). */
+int32_t sdc_last_hip_error(void);
+
+/* SDC_ABI_VERSION of the library. */
+uint32_t sdc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

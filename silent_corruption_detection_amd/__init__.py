@@ -1,0 +1,311 @@
+"""Python binding of libsdc.so -- the MI355X integrity scan for silent data
+corruption checks (see include/sdc.h for the C ABI and the semantics).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  PyTorch provides device memory and streams.  Importing this module
+raises ImportError when the library has not been built; there is no fallback.
+
+Function names are those of the C ABI.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "F32", "BF16", "F16", "COL_SUM", "COL_WSUM", "COL_XOR", "COL_NONFINITE", "COL_ALL",
+    "SdcError", "Plan", "sdc_plan_bytes", "sdc_plan_build", "sdc_fingerprint_plan",
+    "sdc_nonfinite", "sdc_fingerprint", "sdc_majority_ws_bytes", "sdc_majority_compare",
+    "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
+    "sdc_abi_version", "rows_numpy", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
+
+F32, BF16, F16 = 0, 1, 2
+COL_SUM, COL_WSUM, COL_XOR, COL_NONFINITE, COL_ALL = 1, 2, 4, 8, 15
+U64MAX = (1 << 64) - 1
+_TORCH_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("numel", ctypes.c_uint64),
+                ("dtype", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("magic", "n_tensors", "n_items", "n_zero", "total_elems", "total_bytes",
+                 "plan_bytes", "item_bytes")]
+
+
+class _Majority(ctypes.Structure):
+    _fields_ = [("diverged", ctypes.c_int32), ("has_majority", ctypes.c_int32),
+                ("n_diff", ctypes.c_uint64), ("first_diff", ctypes.c_uint64),
+                ("first_no_majority", ctypes.c_uint64)]
+
+
+class _FlipHint(ctypes.Structure):
+    _fields_ = [("index", ctypes.c_uint64), ("bit", ctypes.c_int32), ("dir", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, U64, U32, I32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int32
+    sig = {
+        "sdc_plan_bytes": [P, U64, U64, P],
+        "sdc_plan_build": [P, U64, U64, P, U64, P, P],
+        "sdc_fingerprint_plan": [P, P, P, P],
+        "sdc_nonfinite": [P, P, P, P, P],
+        "sdc_fingerprint": [P, U64, P, U64, P, P],
+        "sdc_majority_ws_bytes": [U32, U64, P],
+        "sdc_majority_compare": [P, U32, U64, U32, P, U64, P, P, P, P],
+        "sdc_diff_ws_bytes": [U64, U64, P],
+        "sdc_fingerprint_diff": [P, P, U64, U32, P, U64, P, P, U64, P, P],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = I32
+    L.sdc_status_string.argtypes = [I32]
+    L.sdc_status_string.restype = ctypes.c_char_p
+    L.sdc_last_hip_error.argtypes = []
+    L.sdc_last_hip_error.restype = I32
+    L.sdc_abi_version.argtypes = []
+    L.sdc_abi_version.restype = U32
+    return L
+
+
+_lib = _load()
+
+
+class SdcError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = _lib.sdc_status_string(status).decode()
+        if status == -5:
+            msg += f" (hipError {_lib.sdc_last_hip_error()})"
+        super().__init__(f"{what}: {msg} [{status}]")
+
+
+def _check(status, what):
+    if status != 0:
+        raise SdcError(status, what)
+
+
+def sdc_status_string(status):
+    return _lib.sdc_status_string(status).decode()
+
+
+def sdc_last_hip_error():
+    return _lib.sdc_last_hip_error()
+
+
+def sdc_abi_version():
+    return _lib.sdc_abi_version()
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _descriptors(tensors, require_contiguous):
+    """Tensor list -> (ctypes array of sdc_tensor, device, kept tensors)."""
+    n = len(tensors)
+    arr = (_Tensor * max(n, 1))()
+    device, keep = None, []
+    for k, t in enumerate(tensors):
+        if t is None:
+            arr[k] = _Tensor(None, 0, F32, 0)
+            continue
+        if t.dtype not in _TORCH_DTYPE:
+            raise TypeError(f"tensor {k}: unsupported dtype {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"tensor {k} is not on a GPU")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"tensor {k} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            if require_contiguous:
+                raise ValueError(f"tensor {k} is not contiguous (a plan reads it in place)")
+            t = t.contiguous()
+        keep.append(t)
+        arr[k] = _Tensor(t.data_ptr() if t.numel() else None, t.numel(), _TORCH_DTYPE[t.dtype], 0)
+    return arr, device, keep
+
+
+def sdc_plan_bytes(tensors, item_bytes=0):
+    arr, _, _ = _descriptors(tensors, require_contiguous=False)
+    b = ctypes.c_uint64(0)
+    _check(_lib.sdc_plan_bytes(arr, len(tensors), item_bytes, ctypes.byref(b)), "sdc_plan_bytes")
+    return b.value
+
+
+class Plan:
+    """A built plan: the device buffer, the host summary and the tensors it reads."""
+
+    def __init__(self, buf, info, tensors, device):
+        self.buf, self.info, self.tensors, self.device = buf, info, tensors, device
+
+    @property
+    def n_tensors(self):
+        return self.info.n_tensors
+
+    @property
+    def total_bytes(self):
+        return self.info.total_bytes
+
+    @property
+    def total_elems(self):
+        return self.info.total_elems
+
+    @property
+    def n_items(self):
+        return self.info.n_items
+
+    @property
+    def item_bytes(self):
+        return self.info.item_bytes
+
+
+def sdc_plan_build(tensors, item_bytes=0, device=None, stream=None):
+    """Builds the work list of a fixed tensor list (synchronous)."""
+    arr, dev, keep = _descriptors(tensors, require_contiguous=True)
+    dev = dev or (torch.device(device) if device is not None else torch.device("cuda"))
+    nbytes = ctypes.c_uint64(0)
+    _check(_lib.sdc_plan_bytes(arr, len(tensors), item_bytes, ctypes.byref(nbytes)),
+           "sdc_plan_bytes")
+    buf = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=dev)
+    info = _PlanInfo()
+    _check(_lib.sdc_plan_build(arr, len(tensors), item_bytes, ctypes.c_void_p(buf.data_ptr()),
+                               buf.numel(), ctypes.byref(info), _stream_handle(stream, dev)),
+           "sdc_plan_build")
+    return Plan(buf, info, keep, dev)
+
+
+def _rows_out(out, n, device):
+    if out is None:
+        return torch.empty((max(n, 0), 4), dtype=torch.int64, device=device)
+    if out.dtype != torch.int64 or out.numel() < 4 * n or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int64 tensor with n*4 elements")
+    return out
+
+
+def sdc_fingerprint_plan(plan, out=None, stream=None):
+    """Rows (sum, wsum, xorsum, nonfinite) of every tensor of the plan, as an
+    int64 [n, 4] device tensor holding the uint64 bit patterns (asynchronous)."""
+    out = _rows_out(out, plan.n_tensors, plan.device)
+    _check(_lib.sdc_fingerprint_plan(ctypes.c_void_p(plan.buf.data_ptr()), ctypes.byref(plan.info),
+                                     ctypes.c_void_p(out.data_ptr()),
+                                     _stream_handle(stream, plan.device)), "sdc_fingerprint_plan")
+    return out
+
+
+def sdc_nonfinite(plan, counts=None, total=None, stream=None):
+    """Per-tensor NaN/Inf counts and their total (int64 device tensors)."""
+    if counts is None:
+        counts = torch.empty(max(plan.n_tensors, 1), dtype=torch.int64, device=plan.device)
+    if total is None:
+        total = torch.empty(1, dtype=torch.int64, device=plan.device)
+    _check(_lib.sdc_nonfinite(ctypes.c_void_p(plan.buf.data_ptr()), ctypes.byref(plan.info),
+                              ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(total.data_ptr()),
+                              _stream_handle(stream, plan.device)), "sdc_nonfinite")
+    return counts[:plan.n_tensors], total
+
+
+def sdc_fingerprint(tensors, out=None, stream=None):
+    """One-shot scan of a tensor list (plan upload synchronous, scan asynchronous)."""
+    arr, dev, keep = _descriptors(tensors, require_contiguous=False)
+    if dev is None:
+        dev = torch.device("cuda")
+    nbytes = ctypes.c_uint64(0)
+    _check(_lib.sdc_plan_bytes(arr, len(tensors), 0, ctypes.byref(nbytes)), "sdc_plan_bytes")
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=dev)
+    out = _rows_out(out, len(tensors), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(_lib.sdc_fingerprint(arr, len(tensors), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream)),
+           "sdc_fingerprint")
+    # keep the workspace and any contiguous copies alive until the scan ran
+    ws.record_stream(s)
+    for t in keep:
+        t.record_stream(s)
+    return out
+
+
+def rows_numpy(rows):
+    """Host uint64 [n, 4] copy of a rows tensor."""
+    return rows.detach().cpu().numpy().view(np.uint64).reshape(-1, 4)
+
+
+def sdc_majority_ws_bytes(R, T):
+    b = ctypes.c_uint64(0)
+    _check(_lib.sdc_majority_ws_bytes(R, T, ctypes.byref(b)), "sdc_majority_ws_bytes")
+    return b.value
+
+
+def sdc_majority_compare(table, R, T=None, col_mask=COL_ALL, tensor_status=None, stream=None):
+    """Strict-majority comparison of a replica-major [R*T, 4] rows tensor
+    (synchronous).  Returns a dict with the summary, the named replicas
+    ("suspects", None when some tensor has no strict majority) and flags."""
+    if T is None:
+        T = table.shape[0] // R
+    if table.dtype != torch.int64 or not table.is_contiguous() or table.numel() < R * T * 4:
+        raise ValueError("table must be a contiguous int64 [R*T, 4] device tensor")
+    dev = table.device
+    ws = torch.empty(max(sdc_majority_ws_bytes(R, T), 1), dtype=torch.uint8, device=dev)
+    res = _Majority()
+    sus = (ctypes.c_uint8 * max(R, 1))()
+    st_ptr = None
+    if tensor_status is not None:
+        if tensor_status.dtype != torch.uint8 or tensor_status.numel() < T:
+            raise ValueError("tensor_status must be a uint8 device tensor of T elements")
+        st_ptr = ctypes.c_void_p(tensor_status.data_ptr())
+    _check(_lib.sdc_majority_compare(ctypes.c_void_p(table.data_ptr()), R, T, col_mask,
+                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.byref(res),
+                                     sus, st_ptr, _stream_handle(stream, dev)),
+           "sdc_majority_compare")
+    flags = np.frombuffer(bytes(sus), dtype=np.uint8)[:R].copy()
+    return {"diverged": bool(res.diverged), "has_majority": bool(res.has_majority),
+            "n_diff": res.n_diff, "first_diff": res.first_diff,
+            "first_no_majority": res.first_no_majority,
+            "suspects": [r for r in range(R) if flags[r]] if res.has_majority else None,
+            "suspect_flags": flags}
+
+
+def sdc_diff_ws_bytes(T, idx_cap):
+    b = ctypes.c_uint64(0)
+    _check(_lib.sdc_diff_ws_bytes(T, idx_cap, ctypes.byref(b)), "sdc_diff_ws_bytes")
+    return b.value
+
+
+def sdc_fingerprint_diff(a, b, col_mask=COL_ALL, idx_cap=None, hints=True, stream=None):
+    """Rows of two [T, 4] rows tensors that differ, ascending, with the
+    single-bit-flip localisation of each (synchronous)."""
+    if a.shape != b.shape or a.dtype != torch.int64 or b.dtype != torch.int64:
+        raise ValueError("a and b must be int64 [T, 4] tensors of the same shape")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    T = a.shape[0]
+    cap = T if idx_cap is None else idx_cap
+    dev = a.device
+    ws = torch.empty(max(sdc_diff_ws_bytes(T, cap), 1), dtype=torch.uint8, device=dev)
+    n = ctypes.c_uint64(0)
+    idx = (ctypes.c_uint64 * max(cap, 1))()
+    hs = (_FlipHint * max(cap, 1))() if hints else None
+    _check(_lib.sdc_fingerprint_diff(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                     T, col_mask, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                     ctypes.byref(n), idx, cap,
+                                     ctypes.cast(hs, ctypes.c_void_p) if hints else None,
+                                     _stream_handle(stream, dev)), "sdc_fingerprint_diff")
+    m = min(n.value, cap)
+    out = {"n_diff": n.value, "indices": [int(idx[i]) for i in range(m)]}
+    if hints:
+        out["hints"] = [(hs[i].index, hs[i].bit, hs[i].dir) for i in range(m)]
+    return out

@@ -1,0 +1,346 @@
+// compare.hip -- comparisons of fingerprint tables on the GPU.
+//
+// sdc_majority_compare: strict-majority comparison of R replicas' tables
+//   (AWS Machine Learning Blog, "Detecting and recovering from silent data
+//   corruption on Amazon SageMaker HyperPod", section "Check 3: Weight
+//   fingerprints, after the optimizer step").  One lane per tensor; the
+//   candidate majority row is found with the Boyer-Moore vote and confirmed
+//   by counting, which decides "more than half" exactly.  Flags and counters
+//   are combined with order-independent atomics (or, min, add).
+// sdc_fingerprint_diff: rows of two tables that differ (same blog, section
+//   "Check 2: Ring replay, before the optimizer step": a replay is compared
+//   bit for bit with the original), reported in ascending order through a
+//   count / scan / write pass, with the single-bit-flip localisation.
+#include <algorithm>
+
+#include "sdc_internal.h"
+
+namespace sdc {
+namespace {
+
+struct Row4 {
+  uint64_t s, w, x, nf;
+};
+
+__device__ __forceinline__ Row4 load_row(const sdc_row* p) {
+  const ulonglong2* q = reinterpret_cast<const ulonglong2*>(p);
+  ulonglong2 a = q[0], b = q[1];
+  return Row4{a.x, a.y, b.x, b.y};
+}
+
+__device__ __forceinline__ bool row_eq(const Row4& a, const Row4& b, uint32_t m) {
+  return (!(m & SDC_COL_SUM) || a.s == b.s) && (!(m & SDC_COL_WSUM) || a.w == b.w) &&
+         (!(m & SDC_COL_XOR) || a.x == b.x) && (!(m & SDC_COL_NONFINITE) || a.nf == b.nf);
+}
+
+bool mask_ok(uint32_t m) { return (m & SDC_COL_ALL) != 0 && (m & ~(uint32_t)SDC_COL_ALL) == 0; }
+
+// ---- majority ----------------------------------------------------------------
+struct MajWS {
+  unsigned long long n_diff, n_nomaj, first_diff, first_nomaj;
+  sdc_majority res;
+  uint32_t pad[4];
+};
+static_assert(sizeof(MajWS) == 80, "majority workspace header");
+
+constexpr uint64_t kMajHdr = 128;
+
+__global__ void __launch_bounds__(kBlock) maj_init(MajWS* ws, uint32_t* sus, uint32_t R) {
+  const uint32_t i0 = blockIdx.x * kBlock + threadIdx.x;
+  if (i0 == 0) {
+    ws->n_diff = 0;
+    ws->n_nomaj = 0;
+    ws->first_diff = ~0ull;
+    ws->first_nomaj = ~0ull;
+  }
+  for (uint32_t r = i0; r < R; r += gridDim.x * kBlock) sus[r] = 0;
+}
+
+__global__ void __launch_bounds__(kBlock) maj_compare(const sdc_row* __restrict__ table, uint32_t R,
+                                                      uint64_t T, uint32_t mask, MajWS* ws,
+                                                      uint32_t* sus, uint8_t* status) {
+  for (uint64_t k = (uint64_t)blockIdx.x * kBlock + threadIdx.x; k < T;
+       k += (uint64_t)gridDim.x * kBlock) {
+    const Row4 r0 = load_row(table + k);
+    bool differs = false;
+    for (uint32_t r = 1; r < R && !differs; ++r)
+      differs = !row_eq(load_row(table + (uint64_t)r * T + k), r0, mask);
+    uint8_t st = 0;
+    if (differs) {
+      // Boyer-Moore vote: if some row is held by more than R/2 replicas it is
+      // the surviving candidate; the count below confirms or rejects it.
+      Row4 cand = r0;
+      uint32_t votes = 1;
+      for (uint32_t r = 1; r < R; ++r) {
+        const Row4 v = load_row(table + (uint64_t)r * T + k);
+        if (votes == 0) {
+          cand = v;
+          votes = 1;
+        } else if (row_eq(v, cand, mask)) {
+          votes++;
+        } else {
+          votes--;
+        }
+      }
+      uint32_t c = 0;
+      for (uint32_t r = 0; r < R; ++r) c += row_eq(load_row(table + (uint64_t)r * T + k), cand, mask);
+      atomicAdd(&ws->n_diff, 1ull);
+      atomicMin(&ws->first_diff, (unsigned long long)k);
+      if (2ull * c > (uint64_t)R) {
+        st = 1;
+        for (uint32_t r = 0; r < R; ++r)
+          if (!row_eq(load_row(table + (uint64_t)r * T + k), cand, mask)) atomicOr(&sus[r], 1u);
+      } else {
+        st = 2;
+        atomicAdd(&ws->n_nomaj, 1ull);
+        atomicMin(&ws->first_nomaj, (unsigned long long)k);
+      }
+    }
+    if (status) status[k] = st;
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) maj_finalize(MajWS* ws, const uint32_t* sus, uint8_t* sus8,
+                                                       uint32_t R) {
+  const bool none = ws->n_nomaj != 0;  // no strict majority somewhere: name no one
+  for (uint32_t r = threadIdx.x; r < R; r += kBlock) sus8[r] = (!none && sus[r]) ? 1 : 0;
+  if (threadIdx.x == 0) {
+    ws->res.diverged = ws->n_diff != 0;
+    ws->res.has_majority = ws->n_nomaj == 0;
+    ws->res.n_diff = ws->n_diff;
+    ws->res.first_diff = ws->first_diff;
+    ws->res.first_no_majority = ws->first_nomaj;
+  }
+}
+
+uint64_t maj_ws_bytes(uint32_t R) {
+  return kMajHdr + ((uint64_t)R * 4 + 255) / 256 * 256 + ((uint64_t)R + 255) / 256 * 256;
+}
+
+// ---- diff --------------------------------------------------------------------
+constexpr uint32_t kPerLane = 4;
+constexpr uint32_t kPerBlock = kBlock * kPerLane;
+
+// Single-bit-flip localisation (see sdc_flip_hint in sdc.h).
+__device__ __forceinline__ sdc_flip_hint flip_hint(const Row4& a, const Row4& b) {
+  sdc_flip_hint h;
+  h.index = ~0ull;
+  h.bit = -1;
+  h.dir = 0;
+  const uint64_t dx = a.x ^ b.x;
+  if (dx == 0 || (dx & (dx - 1)) != 0) return h;
+  const int bit = __ffsll((long long)dx) - 1;
+  const uint64_t ds = b.s - a.s;
+  uint64_t dw = b.w - a.w;
+  int dir;
+  if (ds == dx) {
+    dir = 1;
+  } else if (ds == 0ull - dx) {
+    dir = -1;
+    dw = 0ull - dw;
+  } else {
+    return h;
+  }
+  if (dw >> 63) return h;
+  const uint64_t q = dw >> bit;
+  if (q == 0 || (q << bit) != dw) return h;
+  h.index = q - 1;
+  h.bit = bit;
+  h.dir = dir;
+  return h;
+}
+
+// Exclusive scan of one value per lane over the workgroup; *total gets the sum.
+__device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* total) {
+  __shared__ uint32_t wsum[kWaves];
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t y = __shfl_up(inc, off);
+    if (lane >= (uint32_t)off) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if ((uint32_t)i < wave) before += wsum[i];
+    all += wsum[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+__device__ __forceinline__ uint32_t lane_flags(const sdc_row* a, const sdc_row* b, uint64_t T,
+                                               uint32_t mask, uint64_t k0) {
+  uint32_t f = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < kPerLane; ++j) {
+    const uint64_t k = k0 + j;
+    if (k < T && !row_eq(load_row(a + k), load_row(b + k), mask)) f |= 1u << j;
+  }
+  return f;
+}
+
+__global__ void __launch_bounds__(kBlock) diff_count(const sdc_row* __restrict__ a,
+                                                     const sdc_row* __restrict__ b, uint64_t T,
+                                                     uint32_t mask, unsigned long long* counts) {
+  const uint64_t k0 = (uint64_t)blockIdx.x * kPerBlock + (uint64_t)threadIdx.x * kPerLane;
+  uint32_t tot;
+  block_exscan(__popc(lane_flags(a, b, T, mask, k0)), &tot);
+  if (threadIdx.x == 0) counts[blockIdx.x] = tot;
+}
+
+__global__ void __launch_bounds__(kBlock) diff_scan(const unsigned long long* counts,
+                                                    unsigned long long* offsets, uint64_t nb,
+                                                    unsigned long long* n_diff) {
+  // One workgroup; counts per block are at most kPerBlock, so 64-bit carries.
+  __shared__ unsigned long long carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (uint64_t base = 0; base < nb; base += kBlock) {
+    const uint64_t i = base + threadIdx.x;
+    const uint32_t v = i < nb ? (uint32_t)counts[i] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_exscan(v, &tot);
+    if (i < nb) offsets[i] = carry + ex;
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_diff = carry;
+}
+
+__global__ void __launch_bounds__(kBlock) diff_write(const sdc_row* __restrict__ a,
+                                                     const sdc_row* __restrict__ b, uint64_t T,
+                                                     uint32_t mask,
+                                                     const unsigned long long* offsets,
+                                                     uint64_t* idx, sdc_flip_hint* hints,
+                                                     uint64_t cap) {
+  const uint64_t k0 = (uint64_t)blockIdx.x * kPerBlock + (uint64_t)threadIdx.x * kPerLane;
+  const uint32_t f = lane_flags(a, b, T, mask, k0);
+  uint32_t tot;
+  uint64_t pos = offsets[blockIdx.x] + block_exscan(__popc(f), &tot);
+#pragma unroll
+  for (uint32_t j = 0; j < kPerLane; ++j) {
+    if (!(f & (1u << j))) continue;
+    if (pos < cap) {
+      const uint64_t k = k0 + j;
+      idx[pos] = k;
+      if (hints) hints[pos] = flip_hint(load_row(a + k), load_row(b + k));
+    }
+    pos++;
+  }
+}
+
+struct DiffLayout {
+  uint64_t nb, counts_off, offsets_off, idx_off, hints_off, bytes;
+};
+
+DiffLayout diff_layout(uint64_t T, uint64_t cap) {
+  DiffLayout L;
+  L.nb = (T + kPerBlock - 1) / kPerBlock;
+  L.counts_off = 256;
+  L.offsets_off = L.counts_off + (L.nb * 8 + 255) / 256 * 256;
+  L.idx_off = L.offsets_off + (L.nb * 8 + 255) / 256 * 256;
+  L.hints_off = L.idx_off + (cap * 8 + 255) / 256 * 256;
+  L.bytes = L.hints_off + (cap * sizeof(sdc_flip_hint) + 255) / 256 * 256;
+  return L;
+}
+
+}  // namespace
+}  // namespace sdc
+
+using namespace sdc;
+
+extern "C" int32_t sdc_majority_ws_bytes(uint32_t R, uint64_t T, uint64_t* h_bytes) {
+  if (h_bytes == nullptr || R == 0 || T == 0) return SDC_ERR_INVALID;
+  *h_bytes = maj_ws_bytes(R);
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_majority_compare(const sdc_row* d_table, uint32_t R, uint64_t T,
+                                        uint32_t col_mask, void* d_ws, uint64_t ws_bytes,
+                                        sdc_majority* h_res, uint8_t* h_suspect,
+                                        uint8_t* d_tensor_status, sdc_stream_t stream) {
+  if (d_table == nullptr || R == 0 || T == 0 || h_res == nullptr || h_suspect == nullptr ||
+      d_ws == nullptr || !mask_ok(col_mask))
+    return SDC_ERR_INVALID;
+  if ((uint64_t)R * T / R != T || (uint64_t)R * T >= (1ull << 58)) return SDC_ERR_RANGE;
+  if (ws_bytes < maj_ws_bytes(R)) return SDC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  unsigned char* base = reinterpret_cast<unsigned char*>(d_ws);
+  MajWS* ws = reinterpret_cast<MajWS*>(base);
+  uint32_t* sus = reinterpret_cast<uint32_t*>(base + kMajHdr);
+  uint8_t* sus8 = base + kMajHdr + ((uint64_t)R * 4 + 255) / 256 * 256;
+  const uint32_t gi = (uint32_t)std::min<uint64_t>((R + kBlock - 1) / kBlock, 1024);
+  hipLaunchKernelGGL(maj_init, dim3(gi), dim3(kBlock), 0, s, ws, sus, R);
+  int32_t st = launch_status();
+  if (st) return st;
+  const uint32_t gc = (uint32_t)std::min<uint64_t>((T + kBlock - 1) / kBlock, 4096);
+  hipLaunchKernelGGL(maj_compare, dim3(gc), dim3(kBlock), 0, s, d_table, R, T, col_mask, ws, sus,
+                     d_tensor_status);
+  if ((st = launch_status())) return st;
+  hipLaunchKernelGGL(maj_finalize, dim3(1), dim3(kBlock), 0, s, ws, sus, sus8, R);
+  if ((st = launch_status())) return st;
+  if ((st = hip_status(hipMemcpyAsync(h_res, &ws->res, sizeof(sdc_majority), hipMemcpyDeviceToHost, s))))
+    return st;
+  if ((st = hip_status(hipMemcpyAsync(h_suspect, sus8, R, hipMemcpyDeviceToHost, s)))) return st;
+  return hip_status(hipStreamSynchronize(s));
+}
+
+extern "C" int32_t sdc_diff_ws_bytes(uint64_t T, uint64_t idx_cap, uint64_t* h_bytes) {
+  if (h_bytes == nullptr) return SDC_ERR_INVALID;
+  if (T >= (1ull << 58) || idx_cap >= (1ull << 58)) return SDC_ERR_RANGE;
+  *h_bytes = diff_layout(T, idx_cap).bytes;
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, uint64_t T,
+                                        uint32_t col_mask, void* d_ws, uint64_t ws_bytes,
+                                        uint64_t* h_n_diff, uint64_t* h_idx, uint64_t idx_cap,
+                                        sdc_flip_hint* h_hints, sdc_stream_t stream) {
+  if (h_n_diff == nullptr || !mask_ok(col_mask) || (idx_cap > 0 && h_idx == nullptr))
+    return SDC_ERR_INVALID;
+  if (T == 0) {
+    *h_n_diff = 0;
+    return SDC_OK;
+  }
+  if (d_a == nullptr || d_b == nullptr || d_ws == nullptr) return SDC_ERR_INVALID;
+  if (T >= (1ull << 58) || idx_cap >= (1ull << 58)) return SDC_ERR_RANGE;
+  const DiffLayout L = diff_layout(T, idx_cap);
+  if (ws_bytes < L.bytes) return SDC_ERR_WORKSPACE;
+  if (L.nb > kMaxGrid) return SDC_ERR_RANGE;
+  hipStream_t s = as_stream(stream);
+  unsigned char* base = reinterpret_cast<unsigned char*>(d_ws);
+  unsigned long long* n_diff = reinterpret_cast<unsigned long long*>(base);
+  unsigned long long* counts = reinterpret_cast<unsigned long long*>(base + L.counts_off);
+  unsigned long long* offsets = reinterpret_cast<unsigned long long*>(base + L.offsets_off);
+  uint64_t* idx = reinterpret_cast<uint64_t*>(base + L.idx_off);
+  sdc_flip_hint* hints = reinterpret_cast<sdc_flip_hint*>(base + L.hints_off);
+  int32_t st;
+  hipLaunchKernelGGL(diff_count, dim3((uint32_t)L.nb), dim3(kBlock), 0, s, d_a, d_b, T, col_mask,
+                     counts);
+  if ((st = launch_status())) return st;
+  hipLaunchKernelGGL(diff_scan, dim3(1), dim3(kBlock), 0, s, counts, offsets, L.nb, n_diff);
+  if ((st = launch_status())) return st;
+  hipLaunchKernelGGL(diff_write, dim3((uint32_t)L.nb), dim3(kBlock), 0, s, d_a, d_b, T, col_mask,
+                     offsets, idx, h_hints ? hints : nullptr, idx_cap);
+  if ((st = launch_status())) return st;
+  uint64_t n = 0;
+  if ((st = hip_status(hipMemcpyAsync(&n, n_diff, 8, hipMemcpyDeviceToHost, s)))) return st;
+  if ((st = hip_status(hipStreamSynchronize(s)))) return st;
+  *h_n_diff = n;
+  const uint64_t m = std::min(n, idx_cap);
+  if (m) {
+    if ((st = hip_status(hipMemcpyAsync(h_idx, idx, m * 8, hipMemcpyDeviceToHost, s)))) return st;
+    if (h_hints &&
+        (st = hip_status(hipMemcpyAsync(h_hints, hints, m * sizeof(sdc_flip_hint),
+                                        hipMemcpyDeviceToHost, s))))
+      return st;
+    if ((st = hip_status(hipStreamSynchronize(s)))) return st;
+  }
+  return SDC_OK;
+}

@@ -1,0 +1,101 @@
+"""The C-ABI library loads and exports every declared symbol; host-only entry
+points (sizing, validation, status strings) behave as documented.  No GPU:
+nothing here launches a kernel or touches device memory."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions(header):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sdc_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions(os.path.join(ROOT, "include", "sdc.h"))
+    for required in ("sdc_fingerprint", "sdc_fingerprint_plan", "sdc_plan_build", "sdc_plan_bytes",
+                     "sdc_nonfinite", "sdc_majority_compare", "sdc_fingerprint_diff"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    import silent_corruption_detection_amd as sdc
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    for name in declared_functions(os.path.join(ROOT, "include", "sdc.h")):
+        assert hasattr(lib, name), name
+
+
+def test_oracle_exports_every_declared_symbol():
+    import oracle
+    lib = oracle.lib()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "oracle", "sdc_oracle.h")).read(), flags=re.S)
+    names = set(re.findall(r"\b(oracle_[a-z_0-9]+)\s*\(", text))
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_and_version():
+    import silent_corruption_detection_amd as sdc
+    assert sdc.sdc_abi_version() == 1
+    assert sdc.sdc_status_string(0) == "ok"
+    for code in range(-7, 0):
+        assert sdc.sdc_status_string(code) not in ("ok", "unknown status")
+    assert sdc.sdc_status_string(-99) == "unknown status"
+
+
+class _T(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("numel", ctypes.c_uint64),
+                ("dtype", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+
+
+def plan_bytes(descs, item_bytes=0):
+    import silent_corruption_detection_amd as sdc
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    arr = (_T * max(len(descs), 1))(*[_T(*d) for d in descs])
+    out = ctypes.c_uint64(0)
+    rc = lib.sdc_plan_bytes(arr, ctypes.c_uint64(len(descs)), ctypes.c_uint64(item_bytes),
+                            ctypes.byref(out))
+    return rc, out.value
+
+
+def test_plan_bytes_host_only():
+    # Sizing reads only the descriptors (pointer values are never dereferenced).
+    rc, b0 = plan_bytes([])
+    assert rc == 0 and b0 >= 64
+    rc, b1 = plan_bytes([(0x10000, 1000, 0, 0)])
+    assert rc == 0 and b1 >= 64 + 32
+    # 4 MiB of fp32 split into 64 KiB items: 64 items of 32 bytes each + one cleared row
+    rc, b2 = plan_bytes([(0x10000, 1 << 20, 0, 0)], item_bytes=65536)
+    assert rc == 0 and b2 >= 64 + 64 * 32 + 4
+    # None / empty tensors need no items, only a cleared row
+    rc, b3 = plan_bytes([(None, 0, 0, 0), (0x10000, 0, 1, 0)])
+    assert rc == 0
+
+
+@pytest.mark.parametrize("desc,item_bytes,code", [
+    ((0x10000, 10, 7, 0), 0, -2),      # unknown dtype
+    ((0x10001, 10, 0, 0), 0, -3),      # fp32 pointer not 4-byte aligned
+    ((0x10001, 10, 1, 0), 0, -3),      # bf16 pointer odd
+    ((0x10000, 10, 0, 1), 0, -1),      # flags must be 0
+    ((0x10000, 10, 0, 0), 24, -1),     # item size not a multiple of 16
+    ((0x10000, 10, 0, 0), 8 << 20, -1),  # item size above 4 MiB
+    ((0x10000, 1 << 62, 0, 0), 0, -7),  # too many elements
+])
+def test_plan_validation_errors(desc, item_bytes, code):
+    rc, _ = plan_bytes([desc], item_bytes)
+    assert rc == code
+
+
+def test_workspace_sizing():
+    import silent_corruption_detection_amd as sdc
+    assert sdc.sdc_majority_ws_bytes(3, 100) > 0
+    assert sdc.sdc_diff_ws_bytes(100, 10) > sdc.sdc_diff_ws_bytes(100, 0)
+    with pytest.raises(sdc.SdcError):
+        sdc.sdc_majority_ws_bytes(0, 10)

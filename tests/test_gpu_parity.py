@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path against the oracle, bit for bit, through the C ABI.
+
+Cases: sizes that span several work items and leave ragged heads and tails,
+misaligned starts (tensors carved from a byte buffer at every element-aligned
+offset), item sizes from 16 bytes to 4 MiB (the rows must not depend on how a
+tensor is split), random bit patterns with many NaN/Inf values (the exact
+recount path), large finite bf16 values that trip the packed fp16 pre-check,
+None and empty tensors, and the majority / diff kernels on random tables.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import silent_corruption_detection_amd as sdc
+from _util import assert_rows_equal, oracle_nonfinite, oracle_rows, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ES = {torch.float32: 4, torch.bfloat16: 2, torch.float16: 2}
+SIZES = [1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025,
+         4095, 4096, 4097, 8191, 8193, 65535, 65537, 262143, 262145, 1_000_003]
+
+
+def gen(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def random_bits(nbytes, seed):
+    return torch.randint(0, 256, (max(nbytes, 1),), dtype=torch.uint8, device=DEV,
+                         generator=gen(seed))[:nbytes]
+
+
+def carve(buf, offset, n, dtype):
+    return buf[offset:offset + n * ES[dtype]].view(dtype)
+
+
+def scan(tensors, item_bytes=0):
+    plan = sdc.sdc_plan_build(tensors, item_bytes=item_bytes)
+    out = sdc.sdc_fingerprint_plan(plan)
+    torch.cuda.synchronize()
+    return sdc.rows_numpy(out), plan
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_sizes_and_offsets_random_bits(dtype):
+    es = ES[dtype]
+    for n in SIZES:
+        buf = random_bits(n * es + 16, seed=n)
+        tensors = [carve(buf, off, n, dtype) for off in range(0, 16, es)]
+        say(f"case sizes dtype={dtype} n={n}")
+        rows, _ = scan(tensors)
+        assert_rows_equal(rows, oracle_rows(tensors))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_normal_values_all_item_sizes(dtype):
+    g = gen(11)
+    es = ES[dtype]
+    tensors = []
+    for off, n in ((0, 3_000_017), (es, 1_234_567), (6 * es, 77_777), (2 * es, 5)):
+        buf = torch.zeros(n * es + 16, dtype=torch.uint8, device=DEV)
+        t = carve(buf, off, n, dtype)
+        t.normal_(0, 0.02, generator=g)
+        tensors.append(t)
+    ref = oracle_rows(tensors)
+    for ib in (0, 16, 48, 4096, 65536, 1 << 20, 4 << 20):
+        say(f"case items dtype={dtype} item_bytes={ib}")
+        rows, plan = scan(tensors, item_bytes=ib)
+        assert_rows_equal(rows, ref)
+
+
+def test_misaligned_clone_views_and_nonfinite_patterns():
+    # every NaN/Inf class, in every dtype, at head, body and tail positions
+    specials = {torch.float32: [0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001, 0xFFFFFFFF],
+                torch.bfloat16: [0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0xFFFF],
+                torch.float16: [0x7C00, 0xFC00, 0x7E00, 0x7C01, 0xFFFF]}
+    rng = np.random.default_rng(21)
+    tensors = []
+    for dtype, pats in specials.items():
+        es = ES[dtype]
+        for n in (3, 17, 4099, 300_001):
+            buf = torch.zeros(n * es + 16, dtype=torch.uint8, device=DEV)
+            t = carve(buf, es, n, dtype)
+            t.normal_(0, 0.02, generator=gen(n))
+            iv = t.view(torch.int32 if es == 4 else torch.int16)
+            pos = sorted(set([0, n - 1, n // 2] + rng.integers(0, n, size=min(n, 9)).tolist()))
+            for j, p in enumerate(pos):
+                v = pats[j % len(pats)]
+                iv[p] = v - (1 << (8 * es)) if v >= 1 << (8 * es - 1) else v
+            tensors.append(t)
+    say("case nonfinite patterns")
+    rows, plan = scan(tensors)
+    assert_rows_equal(rows, oracle_rows(tensors))
+    counts, total = sdc.sdc_nonfinite(plan)
+    torch.cuda.synchronize()
+    ref = oracle_nonfinite(tensors)
+    assert counts.cpu().numpy().astype(np.uint64).tolist() == ref.tolist()
+    assert int(total.item()) == int(ref.sum())
+
+
+def test_large_finite_bf16_are_not_counted():
+    # bf16 values with exponent 0xF8..0xFE look like fp16 NaN/Inf to the packed
+    # pre-check; the exact recount must not count them.
+    g = gen(5)
+    t = torch.empty(1 << 20, dtype=torch.bfloat16, device=DEV).normal_(0, 0.02, generator=g)
+    iv = t.view(torch.int16)
+    iv[::97] = 0x7C00 + 0x55   # exponent 0xF8, finite
+    iv[::1013] = 0x7F00        # exponent 0xFE, finite
+    iv[5] = 0x7F80             # +Inf
+    say("case large finite bf16")
+    rows, plan = scan([t])
+    assert_rows_equal(rows, oracle_rows([t]))
+    assert int(rows[0, 3]) == 1
+
+
+def test_none_empty_and_many_tiny_tensors():
+    g = gen(9)
+    rng = np.random.default_rng(9)
+    tensors = []
+    for k in range(5000):
+        kind = k % 7
+        if kind == 0:
+            tensors.append(None)
+        elif kind == 1:
+            tensors.append(torch.empty(0, dtype=torch.float32, device=DEV))
+        else:
+            dt = [torch.float32, torch.bfloat16, torch.float16][int(rng.integers(0, 3))]
+            n = int(rng.integers(1, 40))
+            tensors.append(torch.empty(n, dtype=dt, device=DEV).normal_(0, 1, generator=g))
+    say("case none/empty/tiny")
+    rows, _ = scan(tensors)
+    assert_rows_equal(rows, oracle_rows(tensors))
+    out = sdc.sdc_fingerprint(tensors)  # one-shot form
+    torch.cuda.synchronize()
+    assert_rows_equal(sdc.rows_numpy(out), rows)
+
+
+def test_repeated_scans_and_stale_output_are_overwritten():
+    g = gen(3)
+    ts = [torch.empty(n, dtype=torch.bfloat16, device=DEV).normal_(0, 0.02, generator=g)
+          for n in (5_000_000, 123, 2_000_001)]
+    plan = sdc.sdc_plan_build(ts, item_bytes=65536)
+    out = torch.full((3, 4), -1, dtype=torch.int64, device=DEV)  # garbage must be cleared
+    ref = oracle_rows(ts)
+    for i in range(5):
+        say(f"case repeat {i}")
+        sdc.sdc_fingerprint_plan(plan, out)
+        torch.cuda.synchronize()
+        assert_rows_equal(sdc.rows_numpy(out), ref)
+
+
+def test_plan_errors_are_reported():
+    t = torch.zeros(4, dtype=torch.float32, device=DEV)
+    with pytest.raises(sdc.SdcError):
+        sdc.sdc_plan_build([t], item_bytes=24)  # not a multiple of 16
+    with pytest.raises(ValueError):
+        sdc.sdc_plan_build([t[::2]])  # plans read tensors in place: must be contiguous
+
+
+# ---------------------------------------------------------------------------
+# majority and diff kernels
+# ---------------------------------------------------------------------------
+def random_table(R, T, rng, p_diff=0.3, palette=3):
+    base = rng.integers(0, 1 << 63, size=(T, 4), dtype=np.uint64)
+    alt = rng.integers(0, 1 << 63, size=(palette, T, 4), dtype=np.uint64)
+    table = np.repeat(base[None], R, axis=0)
+    for r in range(R):
+        for k in range(T):
+            if rng.random() < p_diff:
+                c = int(rng.integers(0, palette))
+                col = int(rng.integers(0, 4))
+                table[r, k] = base[k]
+                table[r, k, col] = alt[c, k, col]
+    return table.reshape(R * T, 4)
+
+
+def to_dev(table):
+    return torch.from_numpy(np.ascontiguousarray(table).view(np.int64)).to(DEV)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 7, 16])
+def test_majority_matches_oracle(R):
+    rng = np.random.default_rng(R)
+    for T in (1, 2, 7, 300, 5000):
+        for p in (0.0, 0.01, 0.3):
+            for mask in (O.COL_ALL, O.COL_SUM | O.COL_WSUM, O.COL_XOR):
+                table = random_table(R, T, rng, p)
+                say(f"case majority R={R} T={T} p={p} mask={mask}")
+                status = torch.zeros(T, dtype=torch.uint8, device=DEV)
+                got = sdc.sdc_majority_compare(to_dev(table), R, T, col_mask=mask,
+                                               tensor_status=status)
+                ref = O.majority_compare(table, R, T, mask)
+                for key in ("diverged", "has_majority", "n_diff", "first_diff",
+                            "first_no_majority", "suspects"):
+                    assert got[key] == ref[key], (key, got[key], ref[key])
+                assert np.array_equal(got["suspect_flags"], ref["suspect_flags"])
+                assert np.array_equal(status.cpu().numpy(), ref["tensor_status"])
+
+
+def test_majority_rejects_bad_arguments():
+    t = to_dev(np.zeros((3, 4), dtype=np.uint64))
+    with pytest.raises(sdc.SdcError):
+        sdc.sdc_majority_compare(t, 3, 1, col_mask=0)
+    with pytest.raises(sdc.SdcError):
+        sdc.sdc_majority_compare(t, 3, 1, col_mask=16)
+
+
+def test_diff_matches_oracle():
+    rng = np.random.default_rng(77)
+    for T in (1, 5, 1023, 1024, 1025, 4097, 300_000):
+        a = rng.integers(0, 1 << 63, size=(T, 4), dtype=np.uint64)
+        b = a.copy()
+        nd = int(rng.integers(0, min(T, 50) + 1))
+        hit = rng.choice(T, size=nd, replace=False)
+        for j, k in enumerate(hit):
+            if j % 2 == 0:  # the exact signature of one bit flip
+                i, bit = int(rng.integers(0, 1 << 20)), int(rng.integers(0, 32))
+                d = 1 << bit
+                a[k, 2] &= ~np.uint64(d)
+                b[k, 2] = a[k, 2] | np.uint64(d)
+                b[k, 0] = a[k, 0] + np.uint64(d)
+                b[k, 1] = a[k, 1] + np.uint64((i + 1) * d)
+            else:
+                b[k, int(rng.integers(0, 4))] ^= np.uint64(int(rng.integers(1, 1 << 30)))
+        for mask in (O.COL_ALL, O.COL_SUM | O.COL_WSUM):
+            for cap in (None, 0, 3):
+                say(f"case diff T={T} nd={nd} mask={mask} cap={cap}")
+                got = sdc.sdc_fingerprint_diff(to_dev(a), to_dev(b), col_mask=mask, idx_cap=cap)
+                ref = O.fingerprint_diff(a, b, mask, cap=T if cap is None else cap)
+                assert got["n_diff"] == ref["n_diff"]
+                assert got["indices"] == ref["indices"]
+                assert got["hints"] == ref["hints"]
