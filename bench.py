@@ -1,0 +1,229 @@
+"""Benchmark of the integrity scan on one MI355X.
+
+Default workload: the Llama-70B-shaped bf16 parameter list (723 tensors,
+70,553,706,496 elements, 141.1 GB) scanned in a single pass and compared
+against its stored fingerprint table -- the check run after every optimizer
+step group and after a checkpoint restore.  One step = one fingerprint scan of
+the whole list (clearing launch + scan launch) plus the diff against the
+stored table.  Inputs are resident in HBM before timing starts.
+
+Also reported (same JSON line, "secondary"): the GPT-style ~0.96B fp32
+parameter list with 3 replicas, one step = scan of the 3 replicas + strict-
+majority compare.
+
+Output: one JSON line with the metric, the roofline of the scan kernel
+(algorithmic bytes per launch / launch time from HIP events on the launch
+stream) and the oracle timed on this host's cores on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fingerprint scan GB/s (and % of HBM peak) on ~1B fp32 and 70B bf16 param lists"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCES = ["silent_corruption_detection_amd/csrc/scan.hip",
+                  "silent_corruption_detection_amd/csrc/sdc_internal.h"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per scan launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fingerprint_kernel_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_steps(step, K, W, stream):
+    import torch
+    for _ in range(W):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    return (t1 - t0) * 1000.0 / K, kernel_ms
+
+
+def bench_c5(args, torch, sdc, W_):
+    log("bench: generating the Llama-70B bf16 list (141 GB) ...")
+    w = W_.c5("cuda")
+    plan = sdc.sdc_plan_build(w.tensors)
+    stream = torch.cuda.current_stream()
+    stored = sdc.sdc_fingerprint_plan(plan).clone()  # the fingerprint table stored at checkpoint time
+    out = torch.empty_like(stored)
+    torch.cuda.synchronize()
+    bad = []
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        sdc.sdc_fingerprint_plan(plan, out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        d = sdc.sdc_fingerprint_diff(stored, out, idx_cap=16, stream=stream)
+        if d["n_diff"]:
+            bad.append(d)
+
+    log("bench: timing ...")
+    ms, kms = time_steps(step, args.steps, args.warmup, stream)
+    if bad:
+        raise RuntimeError(f"scan is not reproducible: {bad[:2]}")
+    return w, plan, out, ms, kms
+
+
+def bench_c2(args, torch, sdc, W_):
+    log("bench: generating the GPT-style 0.96B fp32 list x 3 replicas ...")
+    w = W_.c2("cuda")
+    plan = sdc.sdc_plan_build(w.tensors)
+    stream = torch.cuda.current_stream()
+    out = sdc.sdc_fingerprint_plan(plan)
+    torch.cuda.synchronize()
+    res = {}
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        sdc.sdc_fingerprint_plan(plan, out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        res.update(sdc.sdc_majority_compare(out, w.R, w.T, stream=stream))
+
+    ms, kms = time_steps(step, args.steps, args.warmup, stream)
+    if res.get("suspects") != [w.injections[0]["replica"]]:
+        raise RuntimeError(f"majority compare gave {res}")
+    info = dict(workload="gpt_decoder_0.96b_fp32_3_replicas_majority", tensors=w.R * w.T,
+                elements=plan.total_elems, bytes=plan.total_bytes, item_bytes=plan.item_bytes,
+                ms_per_step=round(ms, 4), value=round(plan.total_bytes / ms / 1e6, 1),
+                unit="GB/s", kernel_ms=round(kms, 4),
+                kernel_frac_of_hbm_peak=round(plan.total_bytes / kms / 1e6 / HBM_PEAK_GBS, 4))
+    del w, plan, out
+    return info
+
+
+def cpu_baseline(w, out, budget_s, sdc, torch):
+    """The oracle, single-threaded, on a bounded sample: whole tensors of the
+    same list, in list order from layer 0, until the oracle has run budget_s
+    seconds.  Host copies are made first and not timed.  Also checks the
+    sampled rows against the GPU's."""
+    import numpy as np
+    import oracle as O
+    rows = sdc.rows_numpy(out)
+    order = list(range(1, w.T - 2)) + [0, w.T - 2, w.T - 1]
+    spent, nbytes, nel, n, ok = 0.0, 0, 0, 0, True
+    for k in order:
+        t = w.tensors[k]
+        h = t.detach().reshape(-1).view(torch.uint8).cpu().numpy()
+        t0 = time.perf_counter()
+        r = O.fingerprint(h, O.BF16)
+        spent += time.perf_counter() - t0
+        ok &= bool(np.array_equal(np.array(r, dtype=np.uint64), rows[k]))
+        nbytes += h.nbytes
+        nel += t.numel()
+        n += 1
+        del h
+        if spent >= budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{n} whole tensors of the same list in list order from layer 0 "
+                       f"({nel} elements, {nbytes / 1e9:.2f} GB), single-threaded C oracle, "
+                       f"host copy not timed, {spent:.1f} s"),
+            "elements_per_s": round(nel / spent, 1), "rows_match_gpu": ok}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of single-threaded oracle work in the CPU baseline (0: skip)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan runs on each GPU's own replica and would need only a small "
+              "all-gather of fingerprint tables across GPUs, which is not part of this build)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import silent_corruption_detection_amd as sdc
+    import workloads as W_
+
+    torch.cuda.set_device(0)
+    if args.calib_copy_mib:
+        # an elementwise kernel (not a memcpy): reads n bytes, writes n bytes
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"bench: calibration copy (bitwise_not) of {n} bytes done")
+        del src, dst
+    secondary = None
+    if not args.no_secondary:
+        secondary = bench_c2(args, torch, sdc, W_)
+        torch.cuda.empty_cache()
+    w, plan, out, ms, kms = bench_c5(args, torch, sdc, W_)
+    total_bytes = plan.total_bytes
+    achieved = total_bytes / kms / 1e6  # GB/s
+    traffic = traffic_from_profile("llama70b_bf16")
+    cpu = cpu_baseline(w, out, args.cpu_budget, sdc, torch) if args.cpu_budget > 0 else None
+    value = total_bytes / ms / 1e6
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u64",
+        "data": "synthetic",
+        "config": {"workload": "llama70b_bf16_param_list_single_pass_vs_stored_table",
+                   "data_dtype": "bf16", "tensors": plan.n_tensors, "elements": plan.total_elems,
+                   "bytes": total_bytes, "item_bytes": plan.item_bytes, "work_items": plan.n_items,
+                   "step": "clear + fingerprint scan + diff against the stored table",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "fingerprint_kernel (+ clear_rows_kernel)",
+                     "kernel_ms": round(kms, 4), "kernel_hash": kernel_hash()},
+        "elements_per_s": round(plan.total_elems / ms * 1e3, 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
