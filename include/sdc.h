@@ -97,10 +97,11 @@ typedef struct {
 /* Host-side summary of a plan, filled by sdc_plan_build and passed back to
  * the scan calls (it carries the launch size, so no device read is needed). */
 typedef struct {
-  uint64_t magic;        /* identifies the plan; checked against the device copy */
+  uint64_t magic;        /* identifies a plan built by sdc_plan_build            */
   uint64_t n_tensors;    /* number of descriptors = number of output rows        */
   uint64_t n_items;      /* work items = workgroups of one scan launch           */
-  uint64_t n_zero;       /* rows cleared before each scan                        */
+  uint64_t n_split;      /* rows merged from several items (or missing/empty)    */
+  uint64_t n_slots;      /* partial-row slots in the plan's scratch area         */
   uint64_t total_elems;  /* elements scanned per pass                            */
   uint64_t total_bytes;  /* bytes scanned per pass (the algorithmic traffic)     */
   uint64_t plan_bytes;   /* bytes of the device plan                             */
@@ -134,7 +135,9 @@ int32_t sdc_plan_bytes(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_by
                        uint64_t* h_bytes);
 
 /* Packs the descriptors of h_tensors[0..n) into a work list and copies it into
- * d_plan (plan_bytes bytes of device memory owned by the caller).
+ * d_plan (plan_bytes bytes of device memory owned by the caller).  The plan
+ * also holds the scratch partial rows of tensors split over several work
+ * items, so scans that use the same plan must not overlap in time.
  * SYNCHRONOUS: returns after the copy, ordered on stream, has completed.
  * h_info receives the host summary needed by the scan calls.  The plan stores
  * the tensors' device pointers: they must stay valid while the plan is used.
@@ -145,9 +148,10 @@ int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_by
                        sdc_stream_t stream);
 
 /* [BLOG] "Compare by fingerprint", [AEGIS] xorsum: writes d_out[k] = row of
- * tensor k for k < n_tensors (d_out: n_tensors * 32 bytes of device memory).
- * ASYNCHRONOUS on stream: one clearing launch (if any row is split over
- * several work items) and one scan launch.  Errors: SDC_ERR_INVALID,
+ * tensor k for k < n_tensors (d_out: n_tensors * 32 bytes of device memory;
+ * every row is written, previous contents do not matter).
+ * ASYNCHRONOUS on stream: one scan launch, then one merge launch for the rows
+ * of split (and missing/empty) tensors.  Errors: SDC_ERR_INVALID,
  * SDC_ERR_PLAN, SDC_ERR_HIP. */
 int32_t sdc_fingerprint_plan(const void* d_plan, const sdc_plan_info* h_info, sdc_row* d_out,
                              sdc_stream_t stream);

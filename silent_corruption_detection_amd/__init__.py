@@ -36,8 +36,8 @@ class _Tensor(ctypes.Structure):
 
 class _PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
-                ("magic", "n_tensors", "n_items", "n_zero", "total_elems", "total_bytes",
-                 "plan_bytes", "item_bytes")]
+                ("magic", "n_tensors", "n_items", "n_split", "n_slots", "total_elems",
+                 "total_bytes", "plan_bytes", "item_bytes")]
 
 
 class _Majority(ctypes.Structure):

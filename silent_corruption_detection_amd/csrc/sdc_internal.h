@@ -19,40 +19,70 @@ constexpr uint32_t kVecBytes = 16;
 // = 1024 vectors of 8 elements, so sum_x < 2^29 and sum_(k x) < 2^31.
 constexpr uint64_t kItemBytesMax = 4ull << 20;
 // Automatic item size: aim at this many items, within [kAutoMin, kAutoMax].
-constexpr uint64_t kAutoTargetItems = 16384;
-constexpr uint64_t kAutoMin = 16ull << 10;
+constexpr uint64_t kAutoTargetItems = 65536;
+constexpr uint64_t kAutoMin = 64ull << 10;
 constexpr uint64_t kAutoMax = 1ull << 20;
 constexpr uint64_t kMaxGrid = 0x7FFFFFFFull;
 
 constexpr uint64_t kPlanMagic = 0x31766E6163534453ull;  // "SDScanv1", little-endian
 
-// Item flags.
-constexpr uint32_t kItemWhole = 1u;  // the item is the whole tensor: plain store, no clearing
+// Item flag: the item is the whole tensor, so it stores the tensor's row.
+constexpr uint32_t kItemWhole = 1u << 8;
+constexpr uint32_t kItemDtypeMask = 0xFFu;
 
-// Device plan: [PlanHeader][PlanItem x n_items][uint32 row x n_zero].
+// Device plan, all offsets from the plan's base:
+//   [PlanHeader]
+//   [PlanItem   x n_items]   one per scan workgroup
+//   [PlanSplit  x n_split]   tensors not covered by exactly one item
+//   (pad to 256)
+//   [sdc_row    x n_slots]   partial rows of the items of split tensors
+// The partial rows are scratch written by every scan with this plan.
 struct PlanHeader {
   uint64_t magic;
   uint64_t n_tensors;
   uint64_t n_items;
-  uint64_t n_zero;
-  uint64_t items_off;
-  uint64_t zero_off;
+  uint64_t n_split;
+  uint64_t n_slots;
   uint64_t total_bytes;
   uint64_t item_bytes;
+  uint64_t reserved;
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 
 // One work item: a contiguous element range of one tensor, scanned by one
 // workgroup.  Self-contained so a workgroup needs a single scalar load.
 struct PlanItem {
-  uint64_t addr;   // device address of the item's first element
-  uint64_t start;  // index of that element within its tensor
-  uint32_t len;    // elements in the item
-  uint32_t row;    // output row (tensor index in the list)
-  uint32_t dtype;  // SDC_F32 / SDC_BF16 / SDC_F16
-  uint32_t flags;  // kItemWhole
+  uint64_t addr;         // device address of the item's first element
+  uint64_t start;        // index of that element within its tensor
+  uint32_t len;          // elements in the item
+  uint32_t row;          // output row (tensor index in the list)
+  uint32_t slot;         // partial-row slot (split tensors only)
+  uint32_t dtype_flags;  // SDC_F32 / SDC_BF16 / SDC_F16 | kItemWhole
 };
 static_assert(sizeof(PlanItem) == 32, "plan item layout");
+
+// A tensor whose row is merged from `count` partial rows starting at slot
+// `first` (count 0: a missing or empty tensor, row all zero).
+struct PlanSplit {
+  uint32_t row;
+  uint32_t first;
+  uint32_t count;
+  uint32_t pad;
+};
+static_assert(sizeof(PlanSplit) == 16, "plan split layout");
+
+struct PlanOffsets {
+  uint64_t items, split, partials, end;
+};
+
+inline PlanOffsets plan_offsets(uint64_t n_items, uint64_t n_split, uint64_t n_slots) {
+  PlanOffsets o;
+  o.items = sizeof(PlanHeader);
+  o.split = o.items + n_items * sizeof(PlanItem);
+  o.partials = (o.split + n_split * sizeof(PlanSplit) + 255) / 256 * 256;
+  o.end = o.partials + n_slots * sizeof(sdc_row);
+  return o;
+}
 
 inline uint32_t element_size(uint32_t dtype) {
   return dtype == SDC_F32 ? 4u : (dtype == SDC_BF16 || dtype == SDC_F16) ? 2u : 0u;
