@@ -129,6 +129,50 @@ def bench_c2(args, torch, sdc, W_):
     return info
 
 
+def bench_other(args, torch, sdc, W_, name):
+    """Timing of the other workloads (c1 replicas, c3 gradients + replay, c4
+    small tensors): scan + the comparison each is for, and for c3 the
+    NaN/Inf-count launch on its own."""
+    w = W_.BUILDERS[name]("cuda")
+    plan = sdc.sdc_plan_build(w.tensors)
+    stream = torch.cuda.current_stream()
+    out = sdc.sdc_fingerprint_plan(plan)
+    counts = torch.empty(max(plan.n_tensors, 1), dtype=torch.int64, device="cuda")
+    total = torch.empty(1, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    T = w.T
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        sdc.sdc_fingerprint_plan(plan, out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if name == "c3":
+            sdc.sdc_fingerprint_diff(out[:T], out[T:], stream=stream)
+        else:
+            sdc.sdc_majority_compare(out, w.R, w.T, stream=stream)
+
+    ms, kms = time_steps(step, args.steps, args.warmup, stream)
+    res = dict(workload=w.name, tensors=plan.n_tensors, elements=plan.total_elems,
+               bytes=plan.total_bytes, item_bytes=plan.item_bytes, work_items=plan.n_items,
+               ms_per_step=round(ms, 4), value=round(plan.total_bytes / ms / 1e6, 1), unit="GB/s",
+               kernel_ms=round(kms, 4), kernel_gbs=round(plan.total_bytes / kms / 1e6, 1),
+               kernel_frac_of_hbm_peak=round(plan.total_bytes / kms / 1e6 / HBM_PEAK_GBS, 4))
+    if name == "c3":
+        def nf_step(ev):
+            if ev is not None:
+                ev[0].record(stream)
+            sdc.sdc_nonfinite(plan, counts, total, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        _, nkms = time_steps(nf_step, args.steps, args.warmup, stream)
+        res.update(nonfinite_kernel_ms=round(nkms, 4),
+                   nonfinite_gbs=round(plan.total_bytes / nkms / 1e6, 1),
+                   nonfinite_total=int(total.item()))
+    return res
+
+
 def cpu_baseline(w, out, budget_s, sdc, torch):
     """The oracle, single-threaded, on a bounded sample: whole tensors of the
     same list, in list order from layer 0, until the oracle has run budget_s
@@ -167,6 +211,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of single-threaded oracle work in the CPU baseline (0: skip)")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="c5 (default) prints the benchmark line; the others print their "
+                         "own timing object")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters)")
@@ -193,6 +240,11 @@ def main():
         torch.cuda.synchronize()
         log(f"bench: calibration copy (bitwise_not) of {n} bytes done")
         del src, dst
+    if args.workload != "c5":
+        res = (bench_c2(args, torch, sdc, W_) if args.workload == "c2"
+               else bench_other(args, torch, sdc, W_, args.workload))
+        print(json.dumps(res), flush=True)
+        return
     secondary = None
     if not args.no_secondary:
         secondary = bench_c2(args, torch, sdc, W_)

@@ -99,7 +99,8 @@ typedef struct {
 typedef struct {
   uint64_t magic;        /* identifies a plan built by sdc_plan_build            */
   uint64_t n_tensors;    /* number of descriptors = number of output rows        */
-  uint64_t n_items;      /* work items = workgroups of one scan launch           */
+  uint64_t n_items;      /* work items (workgroup items + wave items)            */
+  uint64_t n_small;      /* of which wave items: small tensors scanned by a wave  */
   uint64_t n_split;      /* rows merged from several items (or missing/empty)    */
   uint64_t n_slots;      /* partial-row slots in the plan's scratch area         */
   uint64_t total_elems;  /* elements scanned per pass                            */
@@ -146,6 +147,18 @@ int32_t sdc_plan_bytes(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_by
 int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
                        void* d_plan, uint64_t plan_bytes, sdc_plan_info* h_info,
                        sdc_stream_t stream);
+
+/* Host-only form of sdc_plan_build for inspection and testing: writes the
+ * plan's descriptor part (everything but the scratch partial rows, i.e. the
+ * first plan_bytes bytes it needs, at most sdc_plan_bytes) to host memory
+ * h_plan and fills h_info.  No HIP call.  Layout of the image: a 64-byte
+ * header {magic, n_tensors, n_items, n_split, n_slots, total_bytes,
+ * item_bytes, n_small} (uint64 each); n_items 32-byte work items {addr u64,
+ * start u64, len u32, row u32, slot u32, dtype | 0x100 if whole-tensor u32},
+ * workgroup items first, then the n_small wave items; then n_split 16-byte
+ * entries {row, first slot, slot count, 0} (uint32 each). */
+int32_t sdc_plan_pack_host(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
+                           void* h_plan, uint64_t plan_bytes, sdc_plan_info* h_info);
 
 /* [BLOG] "Compare by fingerprint", [AEGIS] xorsum: writes d_out[k] = row of
  * tensor k for k < n_tensors (d_out: n_tensors * 32 bytes of device memory;

@@ -170,7 +170,11 @@ struct BodyCfg {
   static constexpr int U = U_;
   static constexpr bool PIPE = PIPE_;
 };
-typedef BodyCfg<4, true> DefaultBody;
+typedef BodyCfg<4, true> DefaultBody;  // 106 VGPRs: 4 workgroups per CU
+typedef BodyCfg<8, true> DeepBody;     // 188 VGPRs: deeper pipeline, 2 workgroups per CU
+// Plans whose items average at least this many bytes use DeepBody (measured:
+// better for items of ~170 KiB and more, worse for lists of small tensors).
+constexpr uint64_t kDeepItemBytes = 96ull << 10;
 // Vectors of the nonfinite-only loop per lane per round.
 constexpr int kUnroll = 4;
 
@@ -264,7 +268,12 @@ __device__ __forceinline__ void scan_scalar(const unsigned char* p, uint32_t j, 
   ln.nf += nonfinite_bits<DT>(x);
 }
 
-__device__ __forceinline__ void block_reduce(Lane& ln) {
+// Index of the calling wave over the grid (4*block + wave), wave-uniform.
+__device__ __forceinline__ uint32_t wave_item_index() {
+  return __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+}
+
+__device__ __forceinline__ void wave_reduce(Lane& ln) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     ln.s += __shfl_xor(ln.s, off);
@@ -272,6 +281,10 @@ __device__ __forceinline__ void block_reduce(Lane& ln) {
     ln.x ^= __shfl_xor(ln.x, off);
     ln.nf += __shfl_xor(ln.nf, off);
   }
+}
+
+__device__ __forceinline__ void block_reduce(Lane& ln) {
+  wave_reduce(ln);
   __shared__ uint64_t ls[kWaves], lw[kWaves];
   __shared__ uint32_t lx[kWaves];
   __shared__ uint64_t ln_[kWaves];
@@ -340,15 +353,88 @@ __global__ void __launch_bounds__(kBlock) fingerprint_kernel(const PlanItem* __r
   d[1] = ulonglong2{(unsigned long long)ln.x, ln.nf};
 }
 
+// ---- wave items: small tensors, one wave each ---------------------------------
+// The aligned body has at most 64 x kWaveVecs vectors; lane l loads vectors
+// 64*u + l for u = 0 .. kWaveVecs-1 all at once (T = kWaveVecs, missing
+// vectors count as zero), then W_lane = (h+1+E*l)*A + 64*E*(T*A - Q) + C.
+template <uint32_t DT>
+__device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane& ln) {
+  typedef typename AccOf<DT>::type Acc;
+  constexpr uint32_t es = (DT == SDC_F32) ? 4u : 2u;
+  constexpr uint32_t E = kVecBytes / es;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(it.addr);
+  const uint32_t len = it.len;
+  const uint32_t mis = (uint32_t)(it.addr & 15u);
+  const uint32_t h = mis ? min(len, (16u - mis) / es) : 0u;
+  const uint32_t nvec = (uint32_t)(((uint64_t)(len - h) * es) / kVecBytes);
+  const uint32_t tail0 = h + nvec * E;
+  const uint32_t ntail = len - tail0;
+  if (l < h) scan_scalar<DT>(base + (uint64_t)l * es, l, ln);
+  if (l >= 32u && l - 32u < ntail) {
+    const uint32_t j = tail0 + (l - 32u);
+    scan_scalar<DT>(base + (uint64_t)j * es, j, ln);
+  }
+  if (nvec) {
+    const unsigned char* body = base + (uint64_t)h * es;
+    __amdgpu_buffer_rsrc_t rs = make_rsrc(body, nvec * kVecBytes);
+    u32x4 v[kWaveVecs];
+#pragma unroll
+    for (uint32_t u = 0; u < kWaveVecs; ++u) {
+      const uint32_t vi = u * 64u + l;
+      v[u] = (vi < nvec) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
+    }
+    Acc acc;
+#pragma unroll
+    for (uint32_t u = 0; u < kWaveVecs; ++u) acc.add(v[u]);
+    const uint64_t T = kWaveVecs;
+    const uint64_t A = acc.sum();
+    ln.s += A;
+    ln.w += (uint64_t)(h + 1u + E * l) * A + (uint64_t)(64u * E) * (T * A - acc.q) + acc.csum();
+    ln.x ^= acc.x;
+    if (acc.flagged()) {  // rare: reload this lane's vectors and count exactly
+      uint32_t c = 0;
+      for (uint32_t vi = l; vi < nvec; vi += 64u) c += nonfinite_vec<DT>(load16(rs, vi * kVecBytes));
+      ln.nf += c;
+    }
+  }
+  wave_reduce(ln);
+  if constexpr (es == 2) ln.x = (ln.x & 0xFFFFu) ^ (ln.x >> 16);
+}
+
+__global__ void __launch_bounds__(kBlock)
+fingerprint_small_kernel(const PlanItem* __restrict__ items,
+                                                                   uint32_t n,
+                                                                   sdc_row* __restrict__ out) {
+  const uint32_t i = wave_item_index();
+  if (i >= n) return;  // the whole wave leaves; no workgroup barrier in this kernel
+  const PlanItem it = items[i];
+  const uint32_t l = threadIdx.x & 63u;
+  Lane ln;
+  switch (it.dtype_flags & kItemDtypeMask) {
+    case SDC_F32: scan_small<SDC_F32>(it, l, ln); break;
+    case SDC_BF16: scan_small<SDC_BF16>(it, l, ln); break;
+    default: scan_small<SDC_F16>(it, l, ln); break;
+  }
+  if (l != 0) return;
+  ulonglong2* d = reinterpret_cast<ulonglong2*>(out + it.row);
+  d[0] = ulonglong2{ln.s, ln.w};
+  d[1] = ulonglong2{(unsigned long long)ln.x, ln.nf};
+}
+
 // Row of each split tensor from its items' partial rows: sums of S and of the
 // already position-offset W (the concatenation identity in additive form),
-// xor of X, sum of NF.  A tensor with no items gets the zero row.
+// xor of X, sum of NF.  A tensor with no items gets the zero row.  One wave
+// per split tensor (entry 4*block + wave).
 __global__ void __launch_bounds__(kBlock) merge_rows_kernel(const PlanSplit* __restrict__ split,
+                                                            uint32_t n_split,
                                                             const sdc_row* __restrict__ partials,
                                                             sdc_row* __restrict__ out) {
-  const PlanSplit sp = split[blockIdx.x];
+  const uint32_t e = wave_item_index();
+  if (e >= n_split) return;
+  const PlanSplit sp = split[e];
+  const uint32_t l = threadIdx.x & 63u;
   Lane ln;
-  for (uint32_t i = threadIdx.x; i < sp.count; i += kBlock) {
+  for (uint32_t i = l; i < sp.count; i += 64u) {
     const ulonglong2* p = reinterpret_cast<const ulonglong2*>(partials + sp.first + i);
     const ulonglong2 a = p[0], b = p[1];
     ln.s += a.x;
@@ -356,8 +442,8 @@ __global__ void __launch_bounds__(kBlock) merge_rows_kernel(const PlanSplit* __r
     ln.x ^= (uint32_t)b.x;
     ln.nf += b.y;
   }
-  block_reduce(ln);
-  if (threadIdx.x != 0) return;
+  wave_reduce(ln);
+  if (l != 0) return;
   ulonglong2* d = reinterpret_cast<ulonglong2*>(out + sp.row);
   d[0] = ulonglong2{ln.s, ln.w};
   d[1] = ulonglong2{(unsigned long long)ln.x, ln.nf};
@@ -470,28 +556,79 @@ __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __res
   if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
 }
 
-__global__ void __launch_bounds__(kBlock) merge_counts_kernel(const PlanSplit* __restrict__ split,
-                                                              const sdc_row* __restrict__ partials,
-                                                              uint64_t* __restrict__ counts) {
-  const PlanSplit sp = split[blockIdx.x];
-  uint64_t c = 0;
-  for (uint32_t i = threadIdx.x; i < sp.count; i += kBlock) c += partials[sp.first + i].nonfinite;
+template <uint32_t DT>
+__device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t l) {
+  constexpr uint32_t es = (DT == SDC_F32) ? 4u : 2u;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(it.addr);
+  const uint32_t len = it.len;
+  const uint32_t mis = (uint32_t)(it.addr & 15u);
+  const uint32_t h = mis ? min(len, (16u - mis) / es) : 0u;
+  const uint32_t nvec = (uint32_t)(((uint64_t)(len - h) * es) / kVecBytes);
+  const uint32_t tail0 = h + nvec * (kVecBytes / es);
+  const uint32_t ntail = len - tail0;
+  uint32_t c = 0;
+  auto scalar = [&](uint32_t j) {
+    const unsigned char* p = base + (uint64_t)j * es;
+    uint32_t x;
+    if constexpr (DT == SDC_F32) x = *reinterpret_cast<const uint32_t*>(p);
+    else x = *reinterpret_cast<const unsigned short*>(p);
+    c += nonfinite_bits<DT>(x);
+  };
+  if (l < h) scalar(l);
+  if (l >= 32u && l - 32u < ntail) scalar(tail0 + (l - 32u));
+  if (nvec) {
+    __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (uint64_t)h * es, nvec * kVecBytes);
+#pragma unroll
+    for (uint32_t u = 0; u < kWaveVecs; ++u) {
+      const uint32_t vi = u * 64u + l;
+      if (vi < nvec) c += nonfinite_vec<DT>(load16(rs, vi * kVecBytes));
+    }
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-  __shared__ uint64_t lc[kWaves];
-  if ((threadIdx.x & 63) == 0) lc[threadIdx.x >> 6] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < kWaves; ++i) c += lc[i];
-    counts[sp.row] = c;
+  return c;
+}
+
+__global__ void __launch_bounds__(kBlock)
+nonfinite_small_kernel(const PlanItem* __restrict__ items,
+                                                                 uint32_t n,
+                                                                 uint64_t* __restrict__ counts,
+                                                                 uint64_t* __restrict__ total) {
+  const uint32_t i = wave_item_index();
+  if (i >= n) return;
+  const PlanItem it = items[i];
+  const uint32_t l = threadIdx.x & 63u;
+  uint32_t c;
+  switch (it.dtype_flags & kItemDtypeMask) {
+    case SDC_F32: c = nonfinite_small<SDC_F32>(it, l); break;
+    case SDC_BF16: c = nonfinite_small<SDC_BF16>(it, l); break;
+    default: c = nonfinite_small<SDC_F16>(it, l); break;
   }
+  if (l != 0) return;
+  if (counts) counts[it.row] = c;
+  if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
+}
+
+__global__ void __launch_bounds__(kBlock) merge_counts_kernel(const PlanSplit* __restrict__ split,
+                                                              uint32_t n_split,
+                                                              const sdc_row* __restrict__ partials,
+                                                              uint64_t* __restrict__ counts) {
+  const uint32_t e = wave_item_index();
+  if (e >= n_split) return;
+  const PlanSplit sp = split[e];
+  const uint32_t l = threadIdx.x & 63u;
+  uint64_t c = 0;
+  for (uint32_t i = l; i < sp.count; i += 64u) c += partials[sp.first + i].nonfinite;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if (l == 0) counts[sp.row] = c;
 }
 
 __global__ void clear_total_kernel(uint64_t* total) { *total = 0; }
 
 // ---- host side: plan layout --------------------------------------------------
 struct Layout {
-  uint64_t n_items = 0, n_split = 0, n_slots = 0, total_elems = 0, total_bytes = 0;
+  uint64_t n_items = 0, n_small = 0, n_split = 0, n_slots = 0, total_elems = 0, total_bytes = 0;
   uint64_t item_bytes = 0;
   PlanOffsets off{};
 };
@@ -520,6 +657,15 @@ uint64_t items_of(uint64_t ptr, uint64_t numel, uint32_t es, uint64_t item_bytes
 
 bool has_data(const sdc_tensor& t) { return t.ptr != nullptr && t.numel != 0; }
 
+// A tensor scanned whole by one wave: it is a single item anyway and its
+// aligned body has at most 64 x kWaveVecs vectors.
+bool is_wave_item(uint64_t ptr, uint64_t numel, uint32_t es, uint64_t item_bytes) {
+  if (items_of(ptr, numel, es, item_bytes) != 1) return false;
+  const uint64_t mis = ptr & 15u;
+  const uint64_t h = mis ? std::min<uint64_t>(numel, (16u - mis) / es) : 0u;
+  return (numel - h) * es / kVecBytes <= kWaveBodyVecs;
+}
+
 int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout* L) {
   if (n > 0 && t == nullptr) return SDC_ERR_INVALID;
   if (n >= (1ull << 31)) return SDC_ERR_RANGE;
@@ -539,15 +685,17 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
     uint64_t ib = align_up(std::max<uint64_t>(bytes / kAutoTargetItems, 1), 4096);
     item_bytes = std::min(kAutoMax, std::max(kAutoMin, ib));
   }
-  uint64_t items = 0, split = 0, slots = 0;
+  uint64_t items = 0, small = 0, split = 0, slots = 0;
   for (uint64_t k = 0; k < n; ++k) {
     if (!has_data(t[k])) {
       split++;
       continue;
     }
-    const uint64_t c = items_of(reinterpret_cast<uintptr_t>(t[k].ptr), t[k].numel,
-                                element_size(t[k].dtype), item_bytes);
+    const uint64_t ptr = reinterpret_cast<uintptr_t>(t[k].ptr);
+    const uint32_t es = element_size(t[k].dtype);
+    const uint64_t c = items_of(ptr, t[k].numel, es, item_bytes);
     items += c;
+    if (is_wave_item(ptr, t[k].numel, es, item_bytes)) small++;
     if (c > 1) {
       split++;
       slots += c;
@@ -555,6 +703,7 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
   }
   if (items > kMaxGrid || slots >= (1ull << 32)) return SDC_ERR_RANGE;
   L->n_items = items;
+  L->n_small = small;
   L->n_split = split;
   L->n_slots = slots;
   L->total_elems = elems;
@@ -565,7 +714,8 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
 }
 
 // Host image of the plan (the partial-row slots are left uninitialised).
-// Items are in list order and address order within each tensor.
+// Workgroup items come first, then wave items; each group is in list order
+// and in address order within a tensor.
 void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<unsigned char>& img) {
   img.assign(L.off.partials, 0);
   PlanHeader* hd = reinterpret_cast<PlanHeader*>(img.data());
@@ -576,9 +726,10 @@ void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<uns
   hd->n_slots = L.n_slots;
   hd->total_bytes = L.total_bytes;
   hd->item_bytes = L.item_bytes;
+  hd->n_small = L.n_small;
   PlanItem* items = reinterpret_cast<PlanItem*>(img.data() + L.off.items);
   PlanSplit* split = reinterpret_cast<PlanSplit*>(img.data() + L.off.split);
-  uint64_t ni = 0, ns = 0, slot = 0;
+  uint64_t ni = 0, nw = L.n_items - L.n_small, ns = 0, slot = 0;
   for (uint64_t k = 0; k < n; ++k) {
     if (!has_data(t[k])) {
       split[ns++] = PlanSplit{(uint32_t)k, 0u, 0u, 0u};
@@ -588,9 +739,10 @@ void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<uns
     const uint64_t ptr = reinterpret_cast<uintptr_t>(t[k].ptr);
     const uint64_t c = items_of(ptr, t[k].numel, es, L.item_bytes);
     const uint32_t whole = (c == 1) ? kItemWhole : 0u;
+    const bool wave = is_wave_item(ptr, t[k].numel, es, L.item_bytes);
     if (c > 1) split[ns++] = PlanSplit{(uint32_t)k, (uint32_t)slot, (uint32_t)c, 0u};
     split_tensor(ptr, t[k].numel, es, L.item_bytes, [&](uint64_t s, uint64_t len) {
-      PlanItem& it = items[ni++];
+      PlanItem& it = items[wave ? nw++ : ni++];
       it.addr = ptr + s * es;
       it.start = s;
       it.len = (uint32_t)len;
@@ -602,7 +754,8 @@ void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<uns
 }
 
 bool info_ok(const sdc_plan_info* h) {
-  if (h == nullptr || h->magic != kPlanMagic || h->n_items > kMaxGrid || h->n_split > h->n_tensors)
+  if (h == nullptr || h->magic != kPlanMagic || h->n_items > kMaxGrid ||
+      h->n_split > h->n_tensors || h->n_small > h->n_items)
     return false;
   return h->plan_bytes >= plan_offsets(h->n_items, h->n_split, h->n_slots).end;
 }
@@ -623,15 +776,25 @@ PlanView view_of(const void* d_plan, const sdc_plan_info* h) {
 
 int32_t launch_scan(const void* d_plan, const sdc_plan_info* h, sdc_row* out, hipStream_t s) {
   const PlanView v = view_of(d_plan, h);
-  if (h->n_items) {
-    hipLaunchKernelGGL(fingerprint_kernel<DefaultBody>, dim3((uint32_t)h->n_items), dim3(kBlock), 0,
-                       s, v.items, v.partials, out);
-    int32_t st = launch_status();
-    if (st) return st;
+  const uint64_t n_block = h->n_items - h->n_small;
+  int32_t st;
+  if (h->n_small) {
+    hipLaunchKernelGGL(fingerprint_small_kernel, dim3((uint32_t)((h->n_small + kWaves - 1) / kWaves)),
+                       dim3(kBlock), 0, s, v.items + n_block, (uint32_t)h->n_small, out);
+    if ((st = launch_status())) return st;
+  }
+  if (n_block) {
+    if (h->total_bytes / h->n_items >= kDeepItemBytes)
+      hipLaunchKernelGGL(fingerprint_kernel<DeepBody>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
+                         v.items, v.partials, out);
+    else
+      hipLaunchKernelGGL(fingerprint_kernel<DefaultBody>, dim3((uint32_t)n_block), dim3(kBlock), 0,
+                         s, v.items, v.partials, out);
+    if ((st = launch_status())) return st;
   }
   if (h->n_split) {
-    hipLaunchKernelGGL(merge_rows_kernel, dim3((uint32_t)h->n_split), dim3(kBlock), 0, s, v.split,
-                       v.partials, out);
+    hipLaunchKernelGGL(merge_rows_kernel, dim3((uint32_t)((h->n_split + kWaves - 1) / kWaves)),
+                       dim3(kBlock), 0, s, v.split, (uint32_t)h->n_split, v.partials, out);
     return launch_status();
   }
   return SDC_OK;
@@ -674,6 +837,34 @@ extern "C" int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint6
   h_info->magic = kPlanMagic;
   h_info->n_tensors = n;
   h_info->n_items = L.n_items;
+  h_info->n_small = L.n_small;
+  h_info->n_split = L.n_split;
+  h_info->n_slots = L.n_slots;
+  h_info->total_elems = L.total_elems;
+  h_info->total_bytes = L.total_bytes;
+  h_info->plan_bytes = L.off.end;
+  h_info->item_bytes = L.item_bytes;
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_plan_pack_host(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
+                                      void* h_plan, uint64_t plan_bytes, sdc_plan_info* h_info) {
+  if (h_plan == nullptr || h_info == nullptr) return SDC_ERR_INVALID;
+  Layout L;
+  int32_t st = layout_plan(h_tensors, n, item_bytes, &L);
+  if (st) return st;
+  if (plan_bytes < L.off.partials) return SDC_ERR_WORKSPACE;
+  std::vector<unsigned char> img;
+  try {
+    pack_plan(h_tensors, n, L, img);
+  } catch (...) {
+    return SDC_ERR_RANGE;
+  }
+  std::memcpy(h_plan, img.data(), img.size());
+  h_info->magic = kPlanMagic;
+  h_info->n_tensors = n;
+  h_info->n_items = L.n_items;
+  h_info->n_small = L.n_small;
   h_info->n_split = L.n_split;
   h_info->n_slots = L.n_slots;
   h_info->total_elems = L.total_elems;
@@ -700,14 +891,22 @@ extern "C" int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info
   hipLaunchKernelGGL(clear_total_kernel, dim3(1), dim3(1), 0, s, d_total);
   int32_t st = launch_status();
   if (st) return st;
-  if (h_info->n_items) {
-    hipLaunchKernelGGL(nonfinite_kernel, dim3((uint32_t)h_info->n_items), dim3(kBlock), 0, s,
-                       v.items, v.partials, d_counts, d_total);
+  const uint64_t n_block = h_info->n_items - h_info->n_small;
+  if (h_info->n_small) {
+    hipLaunchKernelGGL(nonfinite_small_kernel,
+                       dim3((uint32_t)((h_info->n_small + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
+                       v.items + n_block, (uint32_t)h_info->n_small, d_counts, d_total);
+    if ((st = launch_status())) return st;
+  }
+  if (n_block) {
+    hipLaunchKernelGGL(nonfinite_kernel, dim3((uint32_t)n_block), dim3(kBlock), 0, s, v.items,
+                       v.partials, d_counts, d_total);
     if ((st = launch_status())) return st;
   }
   if (d_counts && h_info->n_split) {
-    hipLaunchKernelGGL(merge_counts_kernel, dim3((uint32_t)h_info->n_split), dim3(kBlock), 0, s,
-                       v.split, v.partials, d_counts);
+    hipLaunchKernelGGL(merge_counts_kernel,
+                       dim3((uint32_t)((h_info->n_split + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
+                       v.split, (uint32_t)h_info->n_split, v.partials, d_counts);
     return launch_status();
   }
   return SDC_OK;

@@ -26,13 +26,20 @@ constexpr uint64_t kMaxGrid = 0x7FFFFFFFull;
 
 constexpr uint64_t kPlanMagic = 0x31766E6163534453ull;  // "SDScanv1", little-endian
 
+// Wave items: a tensor whose aligned body is at most kWaveVecs vectors per
+// lane of one wave (64 x 8 x 16 B = 8 KiB) is scanned whole by one wave, with
+// every load of a lane issued at once and a wave-only reduction.
+constexpr uint32_t kWaveVecs = 8;
+constexpr uint32_t kWaveBodyVecs = 64 * kWaveVecs;
+
 // Item flag: the item is the whole tensor, so it stores the tensor's row.
 constexpr uint32_t kItemWhole = 1u << 8;
 constexpr uint32_t kItemDtypeMask = 0xFFu;
 
 // Device plan, all offsets from the plan's base:
 //   [PlanHeader]
-//   [PlanItem   x n_items]   one per scan workgroup
+//   [PlanItem   x n_items]   n_items - n_small workgroup items, then n_small
+//                            wave items
 //   [PlanSplit  x n_split]   tensors not covered by exactly one item
 //   (pad to 256)
 //   [sdc_row    x n_slots]   partial rows of the items of split tensors
@@ -45,7 +52,7 @@ struct PlanHeader {
   uint64_t n_slots;
   uint64_t total_bytes;
   uint64_t item_bytes;
-  uint64_t reserved;
+  uint64_t n_small;
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 
