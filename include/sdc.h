@@ -223,6 +223,52 @@ int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, uint64_t T,
                              void* d_ws, uint64_t ws_bytes, uint64_t* h_n_diff, uint64_t* h_idx,
                              uint64_t idx_cap, sdc_flip_hint* h_hints, sdc_stream_t stream);
 
+/* ---- ring replay audit ([BLOG] "Check 2: Ring replay, before the optimizer
+ * step") --------------------------------------------------------------------
+ * Every rank r replays the work of rank (r + offset) mod n.  The gathered table
+ * holds, per rank, two results of `width` uint64 words each (for example the
+ * loss bits followed by the gradient fingerprint rows): [r][0] = r's own
+ * result, [r][1] = r's replay of its target.  Layout: rank-major,
+ * d_table[(r*2 + j)*width + w]. */
+
+/* Device workspace bytes for sdc_ring_compare (n ranks) and sdc_confirm_verdict. */
+int32_t sdc_ring_ws_bytes(uint32_t n, uint64_t* h_bytes);
+
+/* h_mismatch[r] = 1 when pair r, (target (r+offset) mod n, replayer r),
+ * mismatches: the target's own result differs from r's replay in any word.
+ * SYNCHRONOUS.  Errors: SDC_ERR_INVALID (n == 0, NULL), SDC_ERR_WORKSPACE,
+ * SDC_ERR_RANGE, SDC_ERR_HIP. */
+int32_t sdc_ring_compare(const uint64_t* d_table, uint32_t n, uint64_t width, uint32_t offset,
+                         void* d_ws, uint64_t ws_bytes, uint8_t* h_mismatch, sdc_stream_t stream);
+
+/* Host-only (no HIP call).  h_culprit[q] = 1 for every rank q that appears,
+ * as target or replayer, in at least two mismatched pairs; h_ambiguous[r] = 1
+ * for every mismatched pair r that contains no culprit (it needs
+ * confirmation).  Errors: SDC_ERR_INVALID. */
+int32_t sdc_ring_localize(const uint8_t* h_mismatch, uint32_t n, uint32_t offset,
+                          uint8_t* h_culprit, uint8_t* h_ambiguous);
+
+/* Confirmation of an ambiguous pair: a third GPU (on another node) and the
+ * target replay the target's work once more.  d_third, d_self: those two
+ * replays; d_orig: the target's original own result; d_peer: the replayer's
+ * replay; all `width` words of device memory.  Verdict: the replayer computed
+ * wrong if the third GPU agrees with the original; otherwise, if it agrees
+ * with the replayer, the target is the suspect -- persistent when the target
+ * reproduced its original, transient when its retry agrees with the third
+ * GPU, else unclear; if the third GPU agrees with neither, unattributable.
+ * d_ws: sdc_ring_ws_bytes(1) bytes.  SYNCHRONOUS. */
+enum {
+  SDC_VERDICT_REPLAYER_WRONG = 1, /* suspect: the replayer */
+  SDC_VERDICT_PERSISTENT = 2,     /* suspect: the target   */
+  SDC_VERDICT_TRANSIENT = 3,      /* suspect: the target   */
+  SDC_VERDICT_UNCLEAR = 4,        /* suspect: the target   */
+  SDC_VERDICT_UNATTRIBUTABLE = 5  /* no suspect            */
+};
+int32_t sdc_confirm_verdict(const uint64_t* d_third, const uint64_t* d_self,
+                            const uint64_t* d_orig, const uint64_t* d_peer, uint64_t width,
+                            void* d_ws, uint64_t ws_bytes, int32_t* h_verdict,
+                            sdc_stream_t stream);
+
 /* ---- misc ------------------------------------------------------------------ */
 
 /* Static text for a status code. */

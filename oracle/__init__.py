@@ -5,9 +5,10 @@ A ctypes view of ``libsdc_oracle.so`` (plain single-threaded C, see
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It works on host
 (numpy) buffers only and never touches the HIP library.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-against closed forms, invariants, brute force, library routines and the pages'
-worked example; none is "parity unpinned".
+Parity status: every function here is pinned -- by ``tests/test_oracle_pins.py``
+(closed forms, invariants, brute force, library routines, the pages' worked
+example and fault table) and ``tests/test_ring.py`` (the pages' ring-audit
+scenarios, brute force); none is "parity unpinned".
 """
 import ctypes
 import os
@@ -60,8 +61,12 @@ def lib():
         L.oracle_majority_compare.argtypes = [P, U32, U64, U32, P, P, P]
         L.oracle_flip_hint.argtypes = [P, P, P]
         L.oracle_fingerprint_diff.argtypes = [P, P, U64, U32, P, P, U64, P]
+        L.oracle_ring_pairs.argtypes = [P, U32, U64, U32, P]
+        L.oracle_ring_localize.argtypes = [P, U32, U32, P, P]
+        L.oracle_confirm_verdict.argtypes = [P, P, P, P, U64, P]
         for f in ("oracle_fingerprint", "oracle_fingerprint_list", "oracle_nonfinite_list",
-                  "oracle_majority_compare", "oracle_flip_hint", "oracle_fingerprint_diff"):
+                  "oracle_majority_compare", "oracle_flip_hint", "oracle_fingerprint_diff",
+                  "oracle_ring_pairs", "oracle_ring_localize", "oracle_confirm_verdict"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -182,3 +187,35 @@ def fingerprint_diff(a, b, col_mask=COL_ALL, cap=None):
     m = min(n.value, cap)
     return {"n_diff": n.value, "indices": [int(i) for i in idx[:m]],
             "hints": [(hints[i].index, hints[i].bit, hints[i].dir) for i in range(m)]}
+
+
+VERDICTS = {1: "replayer computed wrong", 2: "persistent", 3: "transient", 4: "unclear",
+            5: "unattributable"}
+
+
+def ring_pairs(table, n, offset):
+    """Mismatch flags of the n ring pairs of an [n, 2, width] uint64 table."""
+    t = np.ascontiguousarray(np.asarray(table, dtype=np.uint64).reshape(n, 2, -1))
+    width = t.shape[2]
+    out = np.zeros(n, dtype=np.uint8)
+    _check(lib().oracle_ring_pairs(t.ctypes.data if t.size else None, n, width, offset,
+                                   out.ctypes.data))
+    return out
+
+
+def ring_localize(mismatch, n, offset):
+    m = np.ascontiguousarray(np.asarray(mismatch, dtype=np.uint8))
+    cul = np.zeros(n, dtype=np.uint8)
+    amb = np.zeros(n, dtype=np.uint8)
+    _check(lib().oracle_ring_localize(m.ctypes.data, n, offset, cul.ctypes.data, amb.ctypes.data))
+    return cul, amb
+
+
+def confirm_verdict(third, self_, orig, peer):
+    arrs = [np.ascontiguousarray(np.asarray(a, dtype=np.uint64).reshape(-1))
+            for a in (third, self_, orig, peer)]
+    width = arrs[0].size
+    v = ctypes.c_int32(0)
+    _check(lib().oracle_confirm_verdict(*[a.ctypes.data if width else None for a in arrs], width,
+                                        ctypes.byref(v)))
+    return v.value

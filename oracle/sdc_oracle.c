@@ -223,3 +223,68 @@ int oracle_fingerprint_diff(const oracle_row* a, const oracle_row* b, uint64_t T
   *n_diff = n;
   return ORACLE_OK;
 }
+
+static int words_equal(const uint64_t* a, const uint64_t* b, uint64_t width) {
+  for (uint64_t i = 0; i < width; ++i)
+    if (a[i] != b[i]) return 0;
+  return 1;
+}
+
+/* "Check 2": every rank replays the rank `offset` positions ahead; pair r
+ * mismatches when the target's own result and the replay are not equal. */
+int oracle_ring_pairs(const uint64_t* table, uint32_t n, uint64_t width, uint32_t offset,
+                      uint8_t* mismatch) {
+  if (n == 0 || mismatch == NULL || (width > 0 && table == NULL)) return ORACLE_EINVAL;
+  for (uint32_t r = 0; r < n; ++r) {
+    uint32_t t = (uint32_t)(((uint64_t)r + offset) % n);
+    const uint64_t* own_of_target = table + ((uint64_t)t * 2 + 0) * width;
+    const uint64_t* replay_by_r = table + ((uint64_t)r * 2 + 1) * width;
+    mismatch[r] = (uint8_t)!words_equal(own_of_target, replay_by_r, width);
+  }
+  return ORACLE_OK;
+}
+
+/* "Check 2": a rank seen in both of its comparisons (or more) is a culprit;
+ * a mismatched pair with no culprit in it is left for confirmation. */
+int oracle_ring_localize(const uint8_t* mismatch, uint32_t n, uint32_t offset, uint8_t* culprit,
+                         uint8_t* ambiguous) {
+  if (n == 0 || mismatch == NULL || culprit == NULL || ambiguous == NULL) return ORACLE_EINVAL;
+  for (uint32_t r = 0; r < n; ++r) culprit[r] = 0;
+  /* count appearances: pair r holds the target (r+offset) mod n and the replayer r */
+  for (uint32_t q = 0; q < n; ++q) {
+    uint32_t hits = 0;
+    for (uint32_t r = 0; r < n; ++r) {
+      if (!mismatch[r]) continue;
+      uint32_t t = (uint32_t)(((uint64_t)r + offset) % n);
+      if (t == q) hits++;
+      if (r == q) hits++;
+    }
+    culprit[q] = (uint8_t)(hits >= 2);
+  }
+  for (uint32_t r = 0; r < n; ++r) {
+    uint32_t t = (uint32_t)(((uint64_t)r + offset) % n);
+    ambiguous[r] = (uint8_t)(mismatch[r] && !culprit[t] && !culprit[r]);
+  }
+  return ORACLE_OK;
+}
+
+/* "Check 2", confirmation: if the third GPU agrees with the target's original
+ * result, the replayer computed wrong; if it agrees with the replayer's
+ * replay, the target is the suspect -- persistent when the target reproduces
+ * its original, transient when its retry matches the third GPU, otherwise
+ * unclear; if the third GPU agrees with neither, no one can be named. */
+int oracle_confirm_verdict(const uint64_t* third, const uint64_t* self, const uint64_t* orig,
+                           const uint64_t* peer, uint64_t width, int32_t* verdict) {
+  if (verdict == NULL || (width > 0 && (third == NULL || self == NULL || orig == NULL || peer == NULL)))
+    return ORACLE_EINVAL;
+  if (words_equal(third, orig, width)) {
+    *verdict = ORACLE_VERDICT_REPLAYER_WRONG;
+  } else if (words_equal(third, peer, width)) {
+    if (words_equal(self, orig, width)) *verdict = ORACLE_VERDICT_PERSISTENT;
+    else if (words_equal(self, third, width)) *verdict = ORACLE_VERDICT_TRANSIENT;
+    else *verdict = ORACLE_VERDICT_UNCLEAR;
+  } else {
+    *verdict = ORACLE_VERDICT_UNATTRIBUTABLE;
+  }
+  return ORACLE_OK;
+}

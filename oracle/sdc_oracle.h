@@ -110,6 +110,34 @@ int oracle_fingerprint_diff(const oracle_row* a, const oracle_row* b, uint64_t T
                             uint32_t col_mask, uint64_t* n_diff, uint64_t* idx, uint64_t cap,
                             oracle_hint* hints);
 
+/* ---- ring replay audit ("Check 2: Ring replay, before the optimizer step") --
+ * table: n ranks x 2 results x width uint64 words, rank-major.  Result 0 of
+ * rank r is r's own result (loss bits and gradient fingerprints), result 1 is
+ * r's replay of rank (r + offset) mod n.  Pair r = (target (r+offset) mod n,
+ * replayer r) mismatches when the target's own result differs from the
+ * replayer's replay in any word. */
+int oracle_ring_pairs(const uint64_t* table, uint32_t n, uint64_t width, uint32_t offset,
+                      uint8_t* mismatch);
+
+/* Culprits are ranks that appear (as target or replayer) in at least two
+ * mismatched pairs; a mismatched pair containing no culprit is ambiguous.
+ * culprit[n] and ambiguous[n] (indexed like mismatch) receive 0/1. */
+int oracle_ring_localize(const uint8_t* mismatch, uint32_t n, uint32_t offset, uint8_t* culprit,
+                         uint8_t* ambiguous);
+
+/* Verdict of a confirmation: a third GPU and the target replay the target's
+ * work again.  third/self: those replays; orig: the target's original own
+ * result; peer: the replayer's replay.  All width words long. */
+enum {
+  ORACLE_VERDICT_REPLAYER_WRONG = 1, /* suspect: the replayer */
+  ORACLE_VERDICT_PERSISTENT = 2,     /* suspect: the target   */
+  ORACLE_VERDICT_TRANSIENT = 3,      /* suspect: the target   */
+  ORACLE_VERDICT_UNCLEAR = 4,        /* suspect: the target   */
+  ORACLE_VERDICT_UNATTRIBUTABLE = 5  /* no suspect            */
+};
+int oracle_confirm_verdict(const uint64_t* third, const uint64_t* self, const uint64_t* orig,
+                           const uint64_t* peer, uint64_t width, int32_t* verdict);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,8 @@ __all__ = [
     "SdcError", "Plan", "sdc_plan_bytes", "sdc_plan_build", "sdc_fingerprint_plan",
     "sdc_nonfinite", "sdc_fingerprint", "sdc_majority_ws_bytes", "sdc_majority_compare",
     "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
-    "sdc_abi_version", "rows_numpy", "LIB_PATH",
+    "sdc_abi_version", "rows_numpy", "LIB_PATH", "sdc_ring_ws_bytes", "sdc_ring_compare",
+    "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
@@ -65,6 +66,11 @@ def _load():
         "sdc_majority_compare": [P, U32, U64, U32, P, U64, P, P, P, P],
         "sdc_diff_ws_bytes": [U64, U64, P],
         "sdc_fingerprint_diff": [P, P, U64, U32, P, U64, P, P, U64, P, P],
+        "sdc_plan_pack_host": [P, U64, U64, P, U64, P],
+        "sdc_ring_ws_bytes": [U32, P],
+        "sdc_ring_compare": [P, U32, U64, U32, P, U64, P, P],
+        "sdc_ring_localize": [P, U32, U32, P, P],
+        "sdc_confirm_verdict": [P, P, P, P, U64, P, U64, P, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -309,3 +315,52 @@ def sdc_fingerprint_diff(a, b, col_mask=COL_ALL, idx_cap=None, hints=True, strea
     if hints:
         out["hints"] = [(hs[i].index, hs[i].bit, hs[i].dir) for i in range(m)]
     return out
+
+
+VERDICTS = {1: "replayer computed wrong", 2: "persistent", 3: "transient", 4: "unclear",
+            5: "unattributable"}
+
+
+def sdc_ring_ws_bytes(n):
+    b = ctypes.c_uint64(0)
+    _check(_lib.sdc_ring_ws_bytes(n, ctypes.byref(b)), "sdc_ring_ws_bytes")
+    return b.value
+
+
+def sdc_ring_compare(table, n, offset, stream=None):
+    """Mismatch flags of the n ring-replay pairs (target (r+offset) mod n,
+    replayer r) of a contiguous int64 device table [n, 2, width] (synchronous)."""
+    if table.dtype != torch.int64 or not table.is_contiguous() or table.numel() % (2 * n):
+        raise ValueError("table must be a contiguous int64 [n, 2, width] device tensor")
+    width = table.numel() // (2 * n)
+    ws = torch.empty(sdc_ring_ws_bytes(n), dtype=torch.uint8, device=table.device)
+    flags = (ctypes.c_uint8 * n)()
+    _check(_lib.sdc_ring_compare(ctypes.c_void_p(table.data_ptr()), n, width, offset,
+                                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), flags,
+                                 _stream_handle(stream, table.device)), "sdc_ring_compare")
+    return np.frombuffer(bytes(flags), dtype=np.uint8).copy()
+
+
+def sdc_ring_localize(mismatch, n, offset):
+    """Host-only: (culprit flags over ranks, ambiguous flags over pairs)."""
+    m = (ctypes.c_uint8 * n)(*[int(x) for x in mismatch])
+    cul = (ctypes.c_uint8 * n)()
+    amb = (ctypes.c_uint8 * n)()
+    _check(_lib.sdc_ring_localize(m, n, offset, cul, amb), "sdc_ring_localize")
+    return (np.frombuffer(bytes(cul), dtype=np.uint8).copy(),
+            np.frombuffer(bytes(amb), dtype=np.uint8).copy())
+
+
+def sdc_confirm_verdict(third, self_, orig, peer, stream=None):
+    """Verdict code (see VERDICTS) of a confirmation from four int64 device vectors."""
+    vs = [third, self_, orig, peer]
+    width = third.numel()
+    for v in vs:
+        if v.dtype != torch.int64 or not v.is_contiguous() or v.numel() != width:
+            raise ValueError("the four results must be contiguous int64 tensors of one length")
+    ws = torch.empty(sdc_ring_ws_bytes(1), dtype=torch.uint8, device=third.device)
+    out = ctypes.c_int32(0)
+    _check(_lib.sdc_confirm_verdict(*[ctypes.c_void_p(v.data_ptr()) for v in vs], width,
+                                    ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.byref(out),
+                                    _stream_handle(stream, third.device)), "sdc_confirm_verdict")
+    return out.value

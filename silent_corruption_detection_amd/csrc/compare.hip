@@ -11,7 +11,10 @@
 //   "Check 2: Ring replay, before the optimizer step": a replay is compared
 //   bit for bit with the original), reported in ascending order through a
 //   count / scan / write pass, with the single-bit-flip localisation.
+// sdc_ring_compare / sdc_ring_localize / sdc_confirm_verdict: the ring replay
+//   audit of the same section over an all-gathered [rank][own, replay] table.
 #include <algorithm>
+#include <vector>
 
 #include "sdc_internal.h"
 
@@ -250,10 +253,122 @@ DiffLayout diff_layout(uint64_t T, uint64_t cap) {
   return L;
 }
 
+// ---- ring replay audit ----------------------------------------------------------
+// Pair r compares the target's own result (row 0 of rank (r+offset) mod n)
+// with the replayer's replay (row 1 of rank r); one workgroup per pair.
+__device__ __forceinline__ uint32_t block_or(uint32_t v) {
+  __shared__ uint32_t w[kWaves];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) all |= w[i];
+  return all;
+}
+
+__global__ void __launch_bounds__(kBlock) ring_compare_kernel(const uint64_t* __restrict__ table,
+                                                              uint32_t n, uint64_t width,
+                                                              uint32_t offset, uint8_t* flags) {
+  const uint32_t r = blockIdx.x;
+  const uint32_t t = (uint32_t)(((uint64_t)r + offset) % n);
+  const uint64_t* own = table + ((uint64_t)t * 2 + 0) * width;
+  const uint64_t* rep = table + ((uint64_t)r * 2 + 1) * width;
+  uint32_t d = 0;
+  for (uint64_t i = threadIdx.x; i < width; i += kBlock) d |= (own[i] != rep[i]);
+  d = block_or(d);
+  if (threadIdx.x == 0) flags[r] = (uint8_t)(d != 0);
+}
+
+// Equality of four vector pairs (third, orig), (third, peer), (self, orig),
+// (self, third): one workgroup each.
+__global__ void __launch_bounds__(kBlock) confirm_kernel(const uint64_t* __restrict__ third,
+                                                         const uint64_t* __restrict__ self,
+                                                         const uint64_t* __restrict__ orig,
+                                                         const uint64_t* __restrict__ peer,
+                                                         uint64_t width, uint8_t* eq) {
+  const uint64_t* a = blockIdx.x < 2 ? third : self;
+  const uint64_t* b = blockIdx.x == 0 ? orig : blockIdx.x == 1 ? peer : blockIdx.x == 2 ? orig : third;
+  uint32_t d = 0;
+  for (uint64_t i = threadIdx.x; i < width; i += kBlock) d |= (a[i] != b[i]);
+  d = block_or(d);
+  if (threadIdx.x == 0) eq[blockIdx.x] = (uint8_t)(d == 0);
+}
+
 }  // namespace
 }  // namespace sdc
 
 using namespace sdc;
+
+extern "C" int32_t sdc_ring_ws_bytes(uint32_t n, uint64_t* h_bytes) {
+  if (h_bytes == nullptr) return SDC_ERR_INVALID;
+  *h_bytes = ((uint64_t)(n < 16 ? 16 : n) + 255) / 256 * 256;
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_ring_compare(const uint64_t* d_table, uint32_t n, uint64_t width,
+                                    uint32_t offset, void* d_ws, uint64_t ws_bytes,
+                                    uint8_t* h_mismatch, sdc_stream_t stream) {
+  if (n == 0 || h_mismatch == nullptr || d_ws == nullptr || (width > 0 && d_table == nullptr))
+    return SDC_ERR_INVALID;
+  if (ws_bytes < n) return SDC_ERR_WORKSPACE;
+  if (width >= (1ull << 56)) return SDC_ERR_RANGE;
+  hipStream_t s = as_stream(stream);
+  uint8_t* flags = reinterpret_cast<uint8_t*>(d_ws);
+  hipLaunchKernelGGL(ring_compare_kernel, dim3(n), dim3(kBlock), 0, s, d_table, n, width, offset,
+                     flags);
+  int32_t st = launch_status();
+  if (st) return st;
+  if ((st = hip_status(hipMemcpyAsync(h_mismatch, flags, n, hipMemcpyDeviceToHost, s)))) return st;
+  return hip_status(hipStreamSynchronize(s));
+}
+
+// Host decision over the mismatch flags (no HIP call): a rank in two or more
+// mismatched pairs is a culprit; a mismatched pair without a culprit is
+// ambiguous and goes to confirmation.
+extern "C" int32_t sdc_ring_localize(const uint8_t* h_mismatch, uint32_t n, uint32_t offset,
+                                     uint8_t* h_culprit, uint8_t* h_ambiguous) {
+  if (n == 0 || h_mismatch == nullptr || h_culprit == nullptr || h_ambiguous == nullptr)
+    return SDC_ERR_INVALID;
+  std::vector<uint32_t> hits(n, 0);
+  for (uint32_t r = 0; r < n; ++r) {
+    if (!h_mismatch[r]) continue;
+    hits[(uint32_t)(((uint64_t)r + offset) % n)]++;
+    hits[r]++;
+  }
+  for (uint32_t q = 0; q < n; ++q) h_culprit[q] = hits[q] >= 2;
+  for (uint32_t r = 0; r < n; ++r) {
+    const uint32_t t = (uint32_t)(((uint64_t)r + offset) % n);
+    h_ambiguous[r] = h_mismatch[r] && !h_culprit[t] && !h_culprit[r];
+  }
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_confirm_verdict(const uint64_t* d_third, const uint64_t* d_self,
+                                       const uint64_t* d_orig, const uint64_t* d_peer,
+                                       uint64_t width, void* d_ws, uint64_t ws_bytes,
+                                       int32_t* h_verdict, sdc_stream_t stream) {
+  if (h_verdict == nullptr || d_ws == nullptr ||
+      (width > 0 && (!d_third || !d_self || !d_orig || !d_peer)))
+    return SDC_ERR_INVALID;
+  if (ws_bytes < 16) return SDC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  uint8_t* eq_d = reinterpret_cast<uint8_t*>(d_ws);
+  hipLaunchKernelGGL(confirm_kernel, dim3(4), dim3(kBlock), 0, s, d_third, d_self, d_orig, d_peer,
+                     width, eq_d);
+  int32_t st = launch_status();
+  if (st) return st;
+  uint8_t eq[4];
+  if ((st = hip_status(hipMemcpyAsync(eq, eq_d, 4, hipMemcpyDeviceToHost, s)))) return st;
+  if ((st = hip_status(hipStreamSynchronize(s)))) return st;
+  // eq: [third == orig, third == peer, self == orig, self == third]
+  if (eq[0]) *h_verdict = SDC_VERDICT_REPLAYER_WRONG;
+  else if (eq[1]) *h_verdict = eq[2] ? SDC_VERDICT_PERSISTENT
+                             : eq[3] ? SDC_VERDICT_TRANSIENT : SDC_VERDICT_UNCLEAR;
+  else *h_verdict = SDC_VERDICT_UNATTRIBUTABLE;
+  return SDC_OK;
+}
 
 extern "C" int32_t sdc_majority_ws_bytes(uint32_t R, uint64_t T, uint64_t* h_bytes) {
   if (h_bytes == nullptr || R == 0 || T == 0) return SDC_ERR_INVALID;
