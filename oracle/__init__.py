@@ -17,8 +17,10 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, F16 = 0, 1, 2
-ESIZE = {F32: 4, BF16: 2, F16: 2}
+F32, BF16, F16, F64, U8, FP8_E4M3, FP8_E5M2, FP8_E4M3FNUZ, FP8_E5M2FNUZ, U16, U32, U64 = range(12)
+ESIZE = {F32: 4, BF16: 2, F16: 2, F64: 8, U8: 1, FP8_E4M3: 1, FP8_E5M2: 1, FP8_E4M3FNUZ: 1,
+         FP8_E5M2FNUZ: 1, U16: 2, U32: 4, U64: 8}
+SIGNED = 1
 COL_SUM, COL_WSUM, COL_XOR, COL_NONFINITE, COL_ALL = 1, 2, 4, 8, 15
 U64MAX = (1 << 64) - 1
 
@@ -56,6 +58,7 @@ def lib():
         L.oracle_is_nonfinite.argtypes = [U64, U32]
         L.oracle_is_nonfinite.restype = ctypes.c_int
         L.oracle_fingerprint.argtypes = [P, U64, U32, P]
+        L.oracle_fingerprint_ex.argtypes = [P, U64, U32, U32, P]
         L.oracle_fingerprint_list.argtypes = [P, P, P, U64, P]
         L.oracle_nonfinite_list.argtypes = [P, P, P, U64, P, P]
         L.oracle_majority_compare.argtypes = [P, U32, U64, U32, P, P, P]
@@ -64,7 +67,7 @@ def lib():
         L.oracle_ring_pairs.argtypes = [P, U32, U64, U32, P]
         L.oracle_ring_localize.argtypes = [P, U32, U32, P, P]
         L.oracle_confirm_verdict.argtypes = [P, P, P, P, U64, P]
-        for f in ("oracle_fingerprint", "oracle_fingerprint_list", "oracle_nonfinite_list",
+        for f in ("oracle_fingerprint", "oracle_fingerprint_ex", "oracle_fingerprint_list", "oracle_nonfinite_list",
                   "oracle_majority_compare", "oracle_flip_hint", "oracle_fingerprint_diff",
                   "oracle_ring_pairs", "oracle_ring_localize", "oracle_confirm_verdict"):
             getattr(L, f).restype = ctypes.c_int
@@ -83,16 +86,16 @@ def _host_bytes(a):
     return a, (a.ctypes.data if a.size else None)
 
 
-def fingerprint(data, dtype):
+def fingerprint(data, dtype, flags=0):
     """Row (S, W, X, NF) of one tensor given as a host numpy array of raw
-    elements (any numpy dtype of the right width; None means a missing tensor)."""
+    elements (any numpy dtype; its bytes are read; None = a missing tensor)."""
     out = Row()
     if data is None:
-        _check(lib().oracle_fingerprint(None, 0, dtype, ctypes.byref(out)))
+        _check(lib().oracle_fingerprint_ex(None, 0, dtype, flags, ctypes.byref(out)))
     else:
         arr, ptr = _host_bytes(data)
         numel = arr.nbytes // ESIZE[dtype]
-        _check(lib().oracle_fingerprint(ptr, numel, dtype, ctypes.byref(out)))
+        _check(lib().oracle_fingerprint_ex(ptr, numel, dtype, flags, ctypes.byref(out)))
     return (out.sum, out.wsum, out.xorsum, out.nonfinite)
 
 

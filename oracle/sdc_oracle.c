@@ -14,9 +14,11 @@
 
 uint32_t oracle_element_size(uint32_t dtype) {
   switch (dtype) {
-    case ORACLE_F32: return 4;
-    case ORACLE_BF16: return 2;
-    case ORACLE_F16: return 2;
+    case ORACLE_F32: case ORACLE_U32: return 4;
+    case ORACLE_BF16: case ORACLE_F16: case ORACLE_U16: return 2;
+    case ORACLE_F64: case ORACLE_U64: return 8;
+    case ORACLE_U8: case ORACLE_FP8_E4M3: case ORACLE_FP8_E5M2:
+    case ORACLE_FP8_E4M3FNUZ: case ORACLE_FP8_E5M2FNUZ: return 1;
     default: return 0;
   }
 }
@@ -32,35 +34,52 @@ static uint64_t load_bits(const unsigned char* base, uint64_t i, uint32_t esize)
   return x;
 }
 
-/* NaN or +-Inf: the exponent field is all ones (every NaN payload and sign
- * counts).  Field positions are those of IEEE binary32, bfloat16 and IEEE
- * binary16. */
+/* NaN or +-Inf.  IEEE-style formats (binary32, bfloat16, binary16, binary64,
+ * fp8 E5M2): the exponent field is all ones (every NaN payload and sign
+ * counts).  fp8 E4M3 (OCP "fn"): no Inf, NaN is S.1111.111.  The "fnuz" fp8
+ * formats: no Inf, the single NaN is 0x80.  Raw integer types: never. */
 int oracle_is_nonfinite(uint64_t x, uint32_t dtype) {
   switch (dtype) {
     case ORACLE_F32: return (x & 0x7F800000ull) == 0x7F800000ull;
     case ORACLE_BF16: return (x & 0x7F80ull) == 0x7F80ull;
     case ORACLE_F16: return (x & 0x7C00ull) == 0x7C00ull;
+    case ORACLE_F64: return (x & 0x7FF0000000000000ull) == 0x7FF0000000000000ull;
+    case ORACLE_FP8_E4M3: return (x & 0x7Full) == 0x7Full;
+    case ORACLE_FP8_E5M2: return (x & 0x7Cull) == 0x7Cull;
+    case ORACLE_FP8_E4M3FNUZ: case ORACLE_FP8_E5M2FNUZ: return x == 0x80ull;
     default: return 0;
   }
+}
+
+/* The pattern x of a `esize`-byte element widened to 64 bits: sign-extended
+ * for 2- and 4-byte elements when ORACLE_SIGNED is set, else zero-extended. */
+static uint64_t widen(uint64_t x, uint32_t esize, uint32_t flags) {
+  if ((flags & ORACLE_SIGNED) && (esize == 2 || esize == 4)) {
+    uint64_t msb = 1ull << (8u * esize - 1u);
+    if (x & msb) x |= ~((msb << 1) - 1u);
+  }
+  return x;
 }
 
 /* "Compare by fingerprint": S = sum of x_i, W = sum of (i+1)*x_i, both modulo
  * 2^64 with 1-based positions; a missing tensor keeps its zero row.
  * AEGIS review, "core method" item 4: X = xor of the x_i.
  * Nonfinite count: the element-exact form of the NaN/Inf test of "Check 1". */
-int oracle_fingerprint(const void* data, uint64_t numel, uint32_t dtype, oracle_row* out) {
-  if (out == NULL) return ORACLE_EINVAL;
+int oracle_fingerprint_ex(const void* data, uint64_t numel, uint32_t dtype, uint32_t flags,
+                          oracle_row* out) {
+  if (out == NULL || (flags & ~(uint32_t)ORACLE_SIGNED) != 0) return ORACLE_EINVAL;
   uint32_t esize = oracle_element_size(dtype);
   if (esize == 0) return ORACLE_EDTYPE;
   uint64_t s = 0, w = 0, x = 0, nf = 0;
   if (data != NULL) {
     const unsigned char* base = (const unsigned char*)data;
     for (uint64_t i = 0; i < numel; ++i) {
-      uint64_t v = load_bits(base, i, esize);
+      uint64_t raw = load_bits(base, i, esize);
+      uint64_t v = widen(raw, esize, flags);
       s += v;
       w += (i + 1) * v;
       x ^= v;
-      nf += (uint64_t)oracle_is_nonfinite(v, dtype);
+      nf += (uint64_t)oracle_is_nonfinite(raw, dtype);
     }
   }
   out->sum = s;
@@ -68,6 +87,10 @@ int oracle_fingerprint(const void* data, uint64_t numel, uint32_t dtype, oracle_
   out->xorsum = x;
   out->nonfinite = nf;
   return ORACLE_OK;
+}
+
+int oracle_fingerprint(const void* data, uint64_t numel, uint32_t dtype, oracle_row* out) {
+  return oracle_fingerprint_ex(data, numel, dtype, 0, out);
 }
 
 int oracle_fingerprint_list(const void* const* ptrs, const uint64_t* numels,

@@ -36,9 +36,21 @@
 extern "C" {
 #endif
 
-/* Element types.  Only the element width and the position of the floating
- * point exponent field matter; values are never interpreted as numbers. */
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+/* Element types.  Only the element width and the NaN/Inf encoding matter;
+ * values are never interpreted as numbers.  The U* types are raw integers
+ * (never NaN/Inf). */
+enum {
+  ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_F64 = 3, ORACLE_U8 = 4,
+  ORACLE_FP8_E4M3 = 5, ORACLE_FP8_E5M2 = 6, ORACLE_FP8_E4M3FNUZ = 7, ORACLE_FP8_E5M2FNUZ = 8,
+  ORACLE_U16 = 9, ORACLE_U32 = 10, ORACLE_U64 = 11
+};
+
+/* Per-tensor flag: widen 2- and 4-byte patterns to 64 bits with sign
+ * extension, as the pages' code does by viewing such elements as int16 and
+ * int32 ("Compare by fingerprint"); 1-byte elements stay unsigned there
+ * (a uint8 view) and 8-byte ones need no widening, so the flag does not
+ * change them.  X is then the xor of the widened values. */
+enum { ORACLE_SIGNED = 1 };
 
 enum {
   ORACLE_OK = 0,
@@ -81,7 +93,10 @@ uint32_t oracle_element_size(uint32_t dtype);
 int oracle_is_nonfinite(uint64_t x, uint32_t dtype);
 
 /* Row of one tensor: data holds numel elements, contiguous, little-endian.
- * data == NULL or numel == 0 gives the zero row. */
+ * data == NULL or numel == 0 gives the zero row.  flags: ORACLE_SIGNED or 0. */
+int oracle_fingerprint_ex(const void* data, uint64_t numel, uint32_t dtype, uint32_t flags,
+                          oracle_row* out);
+/* oracle_fingerprint_ex with flags 0 (zero-extended patterns). */
 int oracle_fingerprint(const void* data, uint64_t numel, uint32_t dtype, oracle_row* out);
 
 /* Rows of n tensors (ptrs[k], numels[k], dtypes[k]) into rows[0..n). */
