@@ -56,9 +56,25 @@ enum {
   SDC_ERR_RANGE = -7      /* a size exceeds what the library supports                   */
 };
 
-/* Element types.  Only the element width (4 or 2 bytes) and the position of
- * the exponent field (for the NaN/Inf count) depend on the type. */
-enum { SDC_F32 = 0, SDC_BF16 = 1, SDC_F16 = 2 };
+/* Element types.  Only the element width (1, 2, 4 or 8 bytes) and the
+ * NaN/Inf encoding (for the nonfinite count) depend on the type; values are
+ * never converted.  NaN/Inf: IEEE formats (F32, BF16, F16, F64, FP8_E5M2):
+ * exponent field all ones; FP8_E4M3 (OCP "fn", no Inf): S.1111.111; the
+ * "fnuz" fp8 formats (no Inf): 0x80; U* raw integers (also int8/bool, int16,
+ * int32, int64 tensors): never. */
+enum {
+  SDC_F32 = 0, SDC_BF16 = 1, SDC_F16 = 2, SDC_F64 = 3, SDC_U8 = 4, SDC_FP8_E4M3 = 5,
+  SDC_FP8_E5M2 = 6, SDC_FP8_E4M3FNUZ = 7, SDC_FP8_E5M2FNUZ = 8, SDC_U16 = 9, SDC_U32 = 10,
+  SDC_U64 = 11
+};
+
+/* sdc_tensor.flags: SDC_FLAG_SIGNED widens 2- and 4-byte patterns with sign
+ * extension before summing, which reproduces [BLOG]'s own fingerprint
+ * function exactly (it views 1/2/4/8-byte elements as uint8/int16/int32/int64
+ * and widens to int64); 1- and 8-byte elements are unaffected.  xorsum is then
+ * the xor of the widened values.  Without the flag every pattern is
+ * zero-extended. */
+enum { SDC_FLAG_SIGNED = 1u };
 
 /* Column mask bits for comparisons.  [BLOG] "Check 3" compares (sum, wsum);
  * SDC_COL_SUM | SDC_COL_WSUM reproduces exactly that comparison. */
@@ -72,8 +88,8 @@ enum {
  *          endian), aligned to the element size; NULL means a missing tensor
  *          (its row is all zero, [BLOG] "Compare by fingerprint").
  *   numel  number of elements (0 gives a zero row); below 2^62.
- *   dtype  SDC_F32, SDC_BF16 or SDC_F16.
- *   flags  must be 0. */
+ *   dtype  one of the SDC_* element types above.
+ *   flags  0 or SDC_FLAG_SIGNED. */
 typedef struct {
   const void* ptr;
   uint64_t numel;
@@ -81,12 +97,13 @@ typedef struct {
   uint32_t flags;
 } sdc_tensor;
 
-/* Fingerprint row of one tensor, x_i = raw bit pattern of element i
- * zero-extended to 64 bits, i = 0 .. numel-1:
+/* Fingerprint row of one tensor, x_i = raw bit pattern of element i widened
+ * to 64 bits (zero-extended; sign-extended for 2-/4-byte elements under
+ * SDC_FLAG_SIGNED), i = 0 .. numel-1:
  *   sum       = sum_i x_i                 mod 2^64   [BLOG] plain sum
  *   wsum      = sum_i (i+1) * x_i         mod 2^64   [BLOG] position-weighted sum
  *   xorsum    = xor_i x_i                            [AEGIS] xorsum
- *   nonfinite = #{i : exponent field of x_i is all ones} (NaN and +-Inf) */
+ *   nonfinite = #{i : element i is NaN or +-Inf in its type's encoding} */
 typedef struct {
   uint64_t sum;
   uint64_t wsum;

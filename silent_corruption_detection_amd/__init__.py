@@ -14,7 +14,8 @@ import numpy as np
 import torch
 
 __all__ = [
-    "F32", "BF16", "F16", "COL_SUM", "COL_WSUM", "COL_XOR", "COL_NONFINITE", "COL_ALL",
+    "F32", "BF16", "F16", "F64", "U8", "FP8_E4M3", "FP8_E5M2", "FP8_E4M3FNUZ", "FP8_E5M2FNUZ",
+    "U16", "U32", "U64", "FLAG_SIGNED", "COL_SUM", "COL_WSUM", "COL_XOR", "COL_NONFINITE", "COL_ALL",
     "SdcError", "Plan", "sdc_plan_bytes", "sdc_plan_build", "sdc_fingerprint_plan",
     "sdc_nonfinite", "sdc_fingerprint", "sdc_majority_ws_bytes", "sdc_majority_compare",
     "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
@@ -24,10 +25,21 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
 
-F32, BF16, F16 = 0, 1, 2
+(F32, BF16, F16, F64, U8, FP8_E4M3, FP8_E5M2, FP8_E4M3FNUZ, FP8_E5M2FNUZ, U16, U32,
+ U64) = range(12)
+FLAG_SIGNED = 1
 COL_SUM, COL_WSUM, COL_XOR, COL_NONFINITE, COL_ALL = 1, 2, 4, 8, 15
 U64MAX = (1 << 64) - 1
-_TORCH_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_TORCH_DTYPE = {
+    torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.float64: F64,
+    torch.uint8: U8, torch.int8: U8, torch.bool: U8,
+    torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: FP8_E5M2,
+    torch.float8_e4m3fnuz: FP8_E4M3FNUZ, torch.float8_e5m2fnuz: FP8_E5M2FNUZ,
+    torch.int16: U16, torch.int32: U32, torch.int64: U64,
+}
+for _name, _code in (("uint16", U16), ("uint32", U32), ("uint64", U64)):
+    if hasattr(torch, _name):
+        _TORCH_DTYPE[getattr(torch, _name)] = _code
 
 
 class _Tensor(ctypes.Structure):
@@ -120,9 +132,12 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _descriptors(tensors, require_contiguous):
-    """Tensor list -> (ctypes array of sdc_tensor, device, kept tensors)."""
+def _descriptors(tensors, require_contiguous, signed=False):
+    """Tensor list -> (ctypes array of sdc_tensor, device, kept tensors).
+    signed: widen 2-/4-byte patterns with sign extension (SDC_FLAG_SIGNED),
+    as the pages' own fingerprint function does."""
     n = len(tensors)
+    flags = FLAG_SIGNED if signed else 0
     arr = (_Tensor * max(n, 1))()
     device, keep = None, []
     for k, t in enumerate(tensors):
@@ -142,7 +157,8 @@ def _descriptors(tensors, require_contiguous):
                 raise ValueError(f"tensor {k} is not contiguous (a plan reads it in place)")
             t = t.contiguous()
         keep.append(t)
-        arr[k] = _Tensor(t.data_ptr() if t.numel() else None, t.numel(), _TORCH_DTYPE[t.dtype], 0)
+        arr[k] = _Tensor(t.data_ptr() if t.numel() else None, t.numel(), _TORCH_DTYPE[t.dtype],
+                         flags)
     return arr, device, keep
 
 
@@ -180,9 +196,9 @@ class Plan:
         return self.info.item_bytes
 
 
-def sdc_plan_build(tensors, item_bytes=0, device=None, stream=None):
+def sdc_plan_build(tensors, item_bytes=0, device=None, stream=None, signed=False):
     """Builds the work list of a fixed tensor list (synchronous)."""
-    arr, dev, keep = _descriptors(tensors, require_contiguous=True)
+    arr, dev, keep = _descriptors(tensors, require_contiguous=True, signed=signed)
     dev = dev or (torch.device(device) if device is not None else torch.device("cuda"))
     nbytes = ctypes.c_uint64(0)
     _check(_lib.sdc_plan_bytes(arr, len(tensors), item_bytes, ctypes.byref(nbytes)),
@@ -225,9 +241,9 @@ def sdc_nonfinite(plan, counts=None, total=None, stream=None):
     return counts[:plan.n_tensors], total
 
 
-def sdc_fingerprint(tensors, out=None, stream=None):
+def sdc_fingerprint(tensors, out=None, stream=None, signed=False):
     """One-shot scan of a tensor list (plan upload synchronous, scan asynchronous)."""
-    arr, dev, keep = _descriptors(tensors, require_contiguous=False)
+    arr, dev, keep = _descriptors(tensors, require_contiguous=False, signed=signed)
     if dev is None:
         dev = torch.device("cuda")
     nbytes = ctypes.c_uint64(0)

@@ -42,6 +42,7 @@ namespace sdc {
 namespace {
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short s2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -49,12 +50,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // avoided on purpose: clang lowers __builtin_bit_cast(T, v.y) as a read of
 // the vector's first component.)
 __device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us2, w); }
+__device__ __forceinline__ s2 as_s2(uint32_t w) { return __builtin_bit_cast(s2, w); }
 __device__ __forceinline__ h2 as_h2(uint32_t w) { return __builtin_bit_cast(h2, w); }
 __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint64_t lohi(uint32_t lo, uint32_t hi) {
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
 
-// acc + lo(d)*lo(w) + hi(d)*hi(w), 16x16 -> 32-bit products, no clamping.
-__device__ __forceinline__ uint32_t dot2(uint32_t d, uint32_t w, uint32_t acc) {
+// acc + lo(d)*lo(w) + hi(d)*hi(w): 16x16 -> 32-bit products (v_dot2_u32_u16 /
+// v_dot2_i32_i16, the latter with sign-extended halves), no clamping.
+__device__ __forceinline__ uint32_t udot2(uint32_t d, uint32_t w, uint32_t acc) {
   return __builtin_amdgcn_udot2(as_us2(d), as_us2(w), acc, false);
+}
+__device__ __forceinline__ int32_t sdot2(uint32_t d, uint32_t w, int32_t acc) {
+  return __builtin_amdgcn_sdot2(as_s2(d), as_s2(w), acc, false);
+}
+// acc + sum over the 4 bytes of d*w (v_dot4_u32_u8).
+__device__ __forceinline__ uint32_t udot4(uint32_t d, uint32_t w, uint32_t acc) {
+  return __builtin_amdgcn_udot4(d, w, acc, false);
 }
 
 // Raw buffer over [base, base + bytes): loads beyond `bytes` return zero.
@@ -72,57 +85,69 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
                             __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kLoadPolicy));
 }
 
-// Exact NaN/Inf tests on raw patterns (exponent field all ones).
-template <uint32_t DT>
-__device__ __forceinline__ uint32_t nonfinite_bits(uint32_t x) {
-  if constexpr (DT == SDC_F32) return (x & 0x7F800000u) == 0x7F800000u;
-  if constexpr (DT == SDC_BF16) return (x & 0x7F80u) == 0x7F80u;
-  return (x & 0x7C00u) == 0x7C00u;  // SDC_F16
+// ---- NaN/Inf ------------------------------------------------------------------
+// Exact rule: an element is NaN/Inf when (x & mask) == val; mask 0: never.
+struct NfRule {
+  uint64_t mask, val;
+};
+
+__device__ __forceinline__ NfRule nf_rule(uint32_t dtype) {
+  switch (dtype) {
+    case SDC_F32: return NfRule{0x7F800000ull, 0x7F800000ull};
+    case SDC_BF16: return NfRule{0x7F80ull, 0x7F80ull};
+    case SDC_F16: return NfRule{0x7C00ull, 0x7C00ull};
+    case SDC_F64: return NfRule{0x7FF0000000000000ull, 0x7FF0000000000000ull};
+    case SDC_FP8_E4M3: return NfRule{0x7Full, 0x7Full};  // no Inf; NaN is S.1111.111
+    case SDC_FP8_E5M2: return NfRule{0x7Cull, 0x7Cull};
+    case SDC_FP8_E4M3FNUZ: case SDC_FP8_E5M2FNUZ: return NfRule{0xFFull, 0x80ull};  // the one NaN
+    default: return NfRule{0ull, 1ull};  // raw integers
+  }
 }
 
-// Exact count of non-finite elements in one 16-byte vector.
-template <uint32_t DT>
-__device__ __forceinline__ uint32_t nonfinite_vec(u32x4 v) {
+__device__ __forceinline__ uint32_t nf_exact(uint64_t x, const NfRule& r) {
+  return (x & r.mask) == r.val;
+}
+
+// Exact count over one 16-byte vector of ES-byte elements.
+template <uint32_t ES>
+__device__ __forceinline__ uint32_t nf_vec(u32x4 v, const NfRule& r) {
   uint32_t c = 0;
-  uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (ES == 8) {
+    c = nf_exact(lohi(d[0], d[1]), r) + nf_exact(lohi(d[2], d[3]), r);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (DT == SDC_F32) {
-      c += nonfinite_bits<DT>(d[i]);
-    } else {
-      c += nonfinite_bits<DT>(d[i] & 0xFFFFu) + nonfinite_bits<DT>(d[i] >> 16);
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (uint32_t b = 0; b < 32; b += 8 * ES) c += nf_exact((d[i] >> b) & ((1ull << (8 * ES)) - 1), r);
     }
   }
   return c;
 }
 
-// Per-lane partial state of one item.
-struct Lane {
-  uint64_t s = 0;   // sum of x over the lane's elements
-  uint64_t w = 0;   // sum of (j+1) x over the lane's elements (j: index in the item)
-  uint32_t x = 0;   // xor of the lane's 32-bit words and scalar elements
-  uint64_t nf = 0;  // exact non-finite count
+// Fast "may contain NaN/Inf" flag, per element-type family.  Every NaN/Inf
+// sets it; a set flag triggers the exact recount, so false alarms only cost
+// time.
+enum : int { kChkNone = 0, kChkHalf = 1, kChkF32 = 2, kChkF64 = 3, kChkFp8Top = 4, kChkFp8Eq = 5 };
+
+template <int CHK>
+struct Chk;
+
+template <>
+struct Chk<kChkNone> {  // raw integers: never NaN/Inf
+  __device__ __forceinline__ explicit Chk(const NfRule&) {}
+  __device__ __forceinline__ void add(u32x4) {}
+  __device__ __forceinline__ bool flagged() const { return false; }
 };
 
-// ---- 16-bit elements (bf16, fp16): 8 per vector ---------------------------
-struct Acc16 {
-  uint32_t a = 0;  // sum x
-  uint32_t c = 0;  // sum k x, k = slot 0..7 in the vector
-  uint64_t q = 0;  // running sum of a after each vector
-  uint32_t x = 0;  // xor of dwords
-  h2 nf = {0, 0};  // sticky NaN flag (+0 until a NaN/Inf is seen)
-
+// bf16 / fp16: fma(x, 0, acc) on the dword read as two fp16 halves stays +0
+// unless a half is fp16 NaN/Inf (exponent bits 14..10 all ones) -- which every
+// fp16 and bf16 NaN/Inf is (for bf16 also finite values >= 2^121).
+template <>
+struct Chk<kChkHalf> {
+  h2 nf = {0, 0};
+  __device__ __forceinline__ explicit Chk(const NfRule&) {}
   __device__ __forceinline__ void add(u32x4 v) {
-    a = dot2(v.x, 0x00010001u, a);
-    a = dot2(v.y, 0x00010001u, a);
-    a = dot2(v.z, 0x00010001u, a);
-    a = dot2(v.w, 0x00010001u, a);
-    c = dot2(v.x, 0x00010000u, c);
-    c = dot2(v.y, 0x00030002u, c);
-    c = dot2(v.z, 0x00050004u, c);
-    c = dot2(v.w, 0x00070006u, c);
-    q += a;
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
     const h2 z = {0, 0};
     nf = __builtin_elementwise_fma(as_h2(v.x), z, nf);
     nf = __builtin_elementwise_fma(as_h2(v.y), z, nf);
@@ -130,37 +155,222 @@ struct Acc16 {
     nf = __builtin_elementwise_fma(as_h2(v.w), z, nf);
   }
   __device__ __forceinline__ bool flagged() const { return h2_bits(nf) != 0; }
-  __device__ __forceinline__ uint64_t sum() const { return a; }
-  __device__ __forceinline__ uint64_t csum() const { return c; }
 };
 
-// ---- 32-bit elements (fp32): 4 per vector ---------------------------------
-struct Acc32 {
-  uint64_t a = 0;  // sum x
-  uint64_t c = 0;  // sum k x, k = slot 0..3
-  uint64_t q = 0;  // running sum of a after each vector
-  uint32_t x = 0;
+template <>
+struct Chk<kChkF32> {  // exact: fma(x, 0, acc) is NaN iff x is NaN/Inf
   float nf = 0.0f;
-
+  __device__ __forceinline__ explicit Chk(const NfRule&) {}
   __device__ __forceinline__ void add(u32x4 v) {
-    a += (uint64_t)v.x + (uint64_t)v.y + (uint64_t)v.z + (uint64_t)v.w;
-    c += (uint64_t)v.y + 2ull * v.z + 3ull * v.w;
-    q += a;
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
     nf = __builtin_fmaf(__uint_as_float(v.x), 0.0f, nf);
     nf = __builtin_fmaf(__uint_as_float(v.y), 0.0f, nf);
     nf = __builtin_fmaf(__uint_as_float(v.z), 0.0f, nf);
     nf = __builtin_fmaf(__uint_as_float(v.w), 0.0f, nf);
   }
   __device__ __forceinline__ bool flagged() const { return __float_as_uint(nf) != 0u; }
+};
+
+template <>
+struct Chk<kChkF64> {  // exact, as for fp32
+  double nf = 0.0;
+  __device__ __forceinline__ explicit Chk(const NfRule&) {}
+  __device__ __forceinline__ void add(u32x4 v) {
+    nf = __builtin_fma(__longlong_as_double((long long)lohi(v.x, v.y)), 0.0, nf);
+    nf = __builtin_fma(__longlong_as_double((long long)lohi(v.z, v.w)), 0.0, nf);
+  }
+  __device__ __forceinline__ bool flagged() const { return __double_as_longlong(nf) != 0; }
+};
+
+// fp8 whose NaN/Inf are "all ones under a mask m < 0x80" (E4M3: m = 0x7F,
+// E5M2: m = 0x7C): per byte, (b & m) + (0x80 - m) reaches 0x80 exactly when
+// (b & m) == m, without carrying into the next byte.  Exact.
+template <>
+struct Chk<kChkFp8Top> {
+  uint32_t flag = 0, m4, k4;
+  __device__ __forceinline__ explicit Chk(const NfRule& r)
+      : m4((uint32_t)r.mask * 0x01010101u), k4((0x80u - (uint32_t)r.mask) * 0x01010101u) {}
+  __device__ __forceinline__ void add(u32x4 v) {
+    flag |= ((v.x & m4) + k4) & 0x80808080u;
+    flag |= ((v.y & m4) + k4) & 0x80808080u;
+    flag |= ((v.z & m4) + k4) & 0x80808080u;
+    flag |= ((v.w & m4) + k4) & 0x80808080u;
+  }
+  __device__ __forceinline__ bool flagged() const { return flag != 0; }
+};
+
+// fp8 "fnuz": the single NaN 0x80; a byte of d ^ 0x80808080 is zero.  Exact.
+template <>
+struct Chk<kChkFp8Eq> {
+  uint32_t flag = 0, v4;
+  __device__ __forceinline__ explicit Chk(const NfRule& r) : v4((uint32_t)r.val * 0x01010101u) {}
+  __device__ __forceinline__ void one(uint32_t d) {
+    const uint32_t t = d ^ v4;
+    flag |= (t - 0x01010101u) & ~t & 0x80808080u;
+  }
+  __device__ __forceinline__ void add(u32x4 v) {
+    one(v.x);
+    one(v.y);
+    one(v.z);
+    one(v.w);
+  }
+  __device__ __forceinline__ bool flagged() const { return flag != 0; }
+};
+
+// ---- per-lane accumulation ------------------------------------------------------
+// Per-lane partial state of one item.
+struct Lane {
+  uint64_t s = 0;   // sum of widened x over the lane's elements
+  uint64_t w = 0;   // sum of (j+1) x over the lane's elements (j: index in the item)
+  uint64_t x = 0;   // xor of the raw words / elements (folded to the width later)
+  uint64_t nf = 0;  // exact non-finite count
+};
+
+// Per vector of E = 16/ES elements: a = sum x, c = sum k x (k = slot in the
+// vector), q = running sum of a after each vector, x = xor of raw words.
+// 32-bit a and c cannot overflow within an item (<= 1024 vectors per lane).
+template <uint32_t ES, bool SIGNED, int CHK>
+struct Acc;
+
+template <bool SIGNED, int CHK>
+struct Acc<1, SIGNED, CHK> {  // 16 bytes per vector; 1-byte elements are never sign-extended
+  uint32_t a = 0, c = 0, x = 0;
+  uint64_t q = 0;
+  Chk<CHK> chk;
+  __device__ __forceinline__ explicit Acc(const NfRule& r) : chk(r) {}
+  __device__ __forceinline__ void add(u32x4 v) {
+    a = udot4(v.x, 0x01010101u, a);
+    a = udot4(v.y, 0x01010101u, a);
+    a = udot4(v.z, 0x01010101u, a);
+    a = udot4(v.w, 0x01010101u, a);
+    c = udot4(v.x, 0x03020100u, c);
+    c = udot4(v.y, 0x07060504u, c);
+    c = udot4(v.z, 0x0B0A0908u, c);
+    c = udot4(v.w, 0x0F0E0D0Cu, c);
+    q += a;
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+    chk.add(v);
+  }
   __device__ __forceinline__ uint64_t sum() const { return a; }
   __device__ __forceinline__ uint64_t csum() const { return c; }
 };
 
-template <uint32_t DT>
-struct AccOf { typedef Acc16 type; };
-template <>
-struct AccOf<SDC_F32> { typedef Acc32 type; };
+template <int CHK>
+struct Acc<2, false, CHK> {
+  uint32_t a = 0, c = 0, x = 0;
+  uint64_t q = 0;
+  Chk<CHK> chk;
+  __device__ __forceinline__ explicit Acc(const NfRule& r) : chk(r) {}
+  __device__ __forceinline__ void add(u32x4 v) {
+    a = udot2(v.x, 0x00010001u, a);
+    a = udot2(v.y, 0x00010001u, a);
+    a = udot2(v.z, 0x00010001u, a);
+    a = udot2(v.w, 0x00010001u, a);
+    c = udot2(v.x, 0x00010000u, c);
+    c = udot2(v.y, 0x00030002u, c);
+    c = udot2(v.z, 0x00050004u, c);
+    c = udot2(v.w, 0x00070006u, c);
+    q += a;
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+    chk.add(v);
+  }
+  __device__ __forceinline__ uint64_t sum() const { return a; }
+  __device__ __forceinline__ uint64_t csum() const { return c; }
+};
+
+template <int CHK>
+struct Acc<2, true, CHK> {  // halves read as int16 (sign-extended products)
+  int32_t a = 0, c = 0;
+  uint32_t x = 0;
+  uint64_t q = 0;
+  Chk<CHK> chk;
+  __device__ __forceinline__ explicit Acc(const NfRule& r) : chk(r) {}
+  __device__ __forceinline__ void add(u32x4 v) {
+    a = sdot2(v.x, 0x00010001u, a);
+    a = sdot2(v.y, 0x00010001u, a);
+    a = sdot2(v.z, 0x00010001u, a);
+    a = sdot2(v.w, 0x00010001u, a);
+    c = sdot2(v.x, 0x00010000u, c);
+    c = sdot2(v.y, 0x00030002u, c);
+    c = sdot2(v.z, 0x00050004u, c);
+    c = sdot2(v.w, 0x00070006u, c);
+    q += (uint64_t)(int64_t)a;
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+    chk.add(v);
+  }
+  __device__ __forceinline__ uint64_t sum() const { return (uint64_t)(int64_t)a; }
+  __device__ __forceinline__ uint64_t csum() const { return (uint64_t)(int64_t)c; }
+};
+
+template <bool SIGNED, int CHK>
+struct Acc<4, SIGNED, CHK> {
+  uint64_t a = 0, c = 0, q = 0;
+  uint32_t x = 0;
+  Chk<CHK> chk;
+  __device__ __forceinline__ explicit Acc(const NfRule& r) : chk(r) {}
+  __device__ __forceinline__ static uint64_t wid(uint32_t v) {
+    if constexpr (SIGNED) return (uint64_t)(int64_t)(int32_t)v;
+    return (uint64_t)v;
+  }
+  __device__ __forceinline__ void add(u32x4 v) {
+    a += wid(v.x) + wid(v.y) + wid(v.z) + wid(v.w);
+    c += wid(v.y) + 2ull * wid(v.z) + 3ull * wid(v.w);
+    q += a;
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+    chk.add(v);
+  }
+  __device__ __forceinline__ uint64_t sum() const { return a; }
+  __device__ __forceinline__ uint64_t csum() const { return c; }
+};
+
+template <bool SIGNED, int CHK>
+struct Acc<8, SIGNED, CHK> {  // 2 elements per vector, full 64-bit patterns
+  uint64_t a = 0, c = 0, q = 0, x = 0;
+  Chk<CHK> chk;
+  __device__ __forceinline__ explicit Acc(const NfRule& r) : chk(r) {}
+  __device__ __forceinline__ void add(u32x4 v) {
+    const uint64_t x0 = lohi(v.x, v.y), x1 = lohi(v.z, v.w);
+    a += x0 + x1;
+    c += x1;
+    q += a;
+    x ^= x0 ^ x1;
+    chk.add(v);
+  }
+  __device__ __forceinline__ uint64_t sum() const { return a; }
+  __device__ __forceinline__ uint64_t csum() const { return c; }
+};
+
+// Element type of an item, resolved once per workgroup (or wave) into the
+// compile-time width / signedness / NaN-check family.
+template <uint32_t ES_, bool SIGNED_, int CHK_>
+struct TypeTag {
+  static constexpr uint32_t ES = ES_;
+  static constexpr bool SIGNED = SIGNED_;
+  static constexpr int CHK = CHK_;
+};
+
+template <class F>
+__device__ __forceinline__ void dispatch_type(uint32_t df, F&& f) {
+  const bool sg = (df & kItemSigned) != 0;
+  switch (df & kItemDtypeMask) {
+    case SDC_F32:
+      if (sg) f(TypeTag<4, true, kChkF32>()); else f(TypeTag<4, false, kChkF32>());
+      break;
+    case SDC_U32:
+      if (sg) f(TypeTag<4, true, kChkNone>()); else f(TypeTag<4, false, kChkNone>());
+      break;
+    case SDC_BF16: case SDC_F16:
+      if (sg) f(TypeTag<2, true, kChkHalf>()); else f(TypeTag<2, false, kChkHalf>());
+      break;
+    case SDC_U16:
+      if (sg) f(TypeTag<2, true, kChkNone>()); else f(TypeTag<2, false, kChkNone>());
+      break;
+    case SDC_F64: f(TypeTag<8, false, kChkF64>()); break;
+    case SDC_U64: f(TypeTag<8, false, kChkNone>()); break;
+    case SDC_FP8_E4M3: case SDC_FP8_E5M2: f(TypeTag<1, false, kChkFp8Top>()); break;
+    case SDC_FP8_E4M3FNUZ: case SDC_FP8_E5M2FNUZ: f(TypeTag<1, false, kChkFp8Eq>()); break;
+    default: f(TypeTag<1, false, kChkNone>()); break;  // SDC_U8
+  }
+}
 
 // Shape of the body loop: U vector loads per lane per round; with PIPE the
 // loads of round r+1 are issued before round r is consumed, so a wave keeps
@@ -170,8 +380,8 @@ struct BodyCfg {
   static constexpr int U = U_;
   static constexpr bool PIPE = PIPE_;
 };
-typedef BodyCfg<4, true> DefaultBody;  // 106 VGPRs: 4 workgroups per CU
-typedef BodyCfg<8, true> DeepBody;     // 188 VGPRs: deeper pipeline, 2 workgroups per CU
+typedef BodyCfg<4, true> DefaultBody;  // ~106 VGPRs: 4 workgroups per CU
+typedef BodyCfg<8, true> DeepBody;     // ~188 VGPRs: deeper pipeline, 2 workgroups per CU
 // Plans whose items average at least this many bytes use DeepBody (measured:
 // better for items of ~170 KiB and more, worse for lists of small tensors).
 constexpr uint64_t kDeepItemBytes = 96ull << 10;
@@ -206,15 +416,15 @@ __device__ __forceinline__ void load_round(const unsigned char* body, uint32_t n
 // 256*it + t, it = 0 .. T-1 with T = rounds*U (uniform over the workgroup);
 // vectors past the end are not loaded and count as zero vectors, which leave
 // every partial sum unchanged (and keep T*A - Q exact).
-template <uint32_t DT, class Cfg>
+template <class Ty, class Cfg>
 __device__ __forceinline__ void scan_body(const unsigned char* body, uint32_t nvec, uint32_t h,
-                                          Lane& ln) {
-  typedef typename AccOf<DT>::type Acc;
+                                          const NfRule& rule, Lane& ln) {
+  typedef Acc<Ty::ES, Ty::SIGNED, Ty::CHK> A_t;
   constexpr int U = Cfg::U;
-  constexpr uint32_t E = (DT == SDC_F32) ? 4u : 8u;  // elements per vector
-  constexpr uint32_t kRound = kBlock * U;            // vectors per round
+  constexpr uint32_t E = kVecBytes / Ty::ES;    // elements per vector
+  constexpr uint32_t kRound = kBlock * U;      // vectors per round
   const uint32_t t = threadIdx.x;
-  Acc acc;
+  A_t acc(rule);
   const uint32_t full = nvec / kRound;
   const uint32_t rounds = full + ((nvec % kRound) ? 1u : 0u);
   if constexpr (!Cfg::PIPE) {
@@ -245,27 +455,55 @@ __device__ __forceinline__ void scan_body(const unsigned char* body, uint32_t nv
   ln.s += A;
   ln.w += (uint64_t)(h + 1u + E * t) * A + (uint64_t)(kBlock * E) * (T * A - acc.q) + acc.csum();
   ln.x ^= acc.x;
-  if (acc.flagged()) {
+  if (acc.chk.flagged()) {
     // Rare: some element may be NaN/Inf.  Recount this lane's vectors exactly.
     uint32_t c = 0;
     for (uint32_t vi = t; vi < nvec; vi += kBlock) {
       __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
-      c += nonfinite_vec<DT>(load16(rs, 0));
+      c += nf_vec<Ty::ES>(load16(rs, 0), rule);
     }
     ln.nf += c;
   }
 }
 
+// Raw pattern of the ES-byte element at p.
+template <uint32_t ES>
+__device__ __forceinline__ uint64_t load_elem(const unsigned char* p) {
+  if constexpr (ES == 1) return *p;
+  if constexpr (ES == 2) return *reinterpret_cast<const unsigned short*>(p);
+  if constexpr (ES == 4) return *reinterpret_cast<const uint32_t*>(p);
+  return *reinterpret_cast<const uint64_t*>(p);
+}
+
+template <uint32_t ES, bool SIGNED>
+__device__ __forceinline__ uint64_t widen(uint64_t raw) {
+  if constexpr (SIGNED && ES == 2) return (uint64_t)(int64_t)(int16_t)(uint16_t)raw;
+  if constexpr (SIGNED && ES == 4) return (uint64_t)(int64_t)(int32_t)(uint32_t)raw;
+  return raw;
+}
+
 // Head/tail element j (index within the item) at p.
-template <uint32_t DT>
-__device__ __forceinline__ void scan_scalar(const unsigned char* p, uint32_t j, Lane& ln) {
-  uint32_t x;
-  if constexpr (DT == SDC_F32) x = *reinterpret_cast<const uint32_t*>(p);
-  else x = *reinterpret_cast<const unsigned short*>(p);
-  ln.s += x;
-  ln.w += (uint64_t)(j + 1u) * x;
-  ln.x ^= x;
-  ln.nf += nonfinite_bits<DT>(x);
+template <class Ty>
+__device__ __forceinline__ void scan_scalar(const unsigned char* p, uint32_t j, const NfRule& rule,
+                                            Lane& ln) {
+  const uint64_t raw = load_elem<Ty::ES>(p);
+  const uint64_t v = widen<Ty::ES, Ty::SIGNED>(raw);
+  ln.s += v;
+  ln.w += (uint64_t)(j + 1u) * v;
+  ln.x ^= raw;
+  if constexpr (Ty::CHK != kChkNone) ln.nf += nf_exact(raw, rule);
+}
+
+// xor of raw words -> xor of the elements' widened patterns.
+template <class Ty>
+__device__ __forceinline__ uint64_t finish_xor(uint64_t x) {
+  if constexpr (Ty::ES == 1) {
+    x ^= x >> 16;
+    x = (x ^ (x >> 8)) & 0xFFu;
+  } else if constexpr (Ty::ES == 2) {
+    x = (x & 0xFFFFu) ^ (x >> 16);
+  }
+  return widen<Ty::ES, Ty::SIGNED>(x);
 }
 
 // Index of the calling wave over the grid (4*block + wave), wave-uniform.
@@ -285,9 +523,7 @@ __device__ __forceinline__ void wave_reduce(Lane& ln) {
 
 __device__ __forceinline__ void block_reduce(Lane& ln) {
   wave_reduce(ln);
-  __shared__ uint64_t ls[kWaves], lw[kWaves];
-  __shared__ uint32_t lx[kWaves];
-  __shared__ uint64_t ln_[kWaves];
+  __shared__ uint64_t ls[kWaves], lw[kWaves], lx[kWaves], ln_[kWaves];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     ls[wave] = ln.s;
@@ -307,27 +543,41 @@ __device__ __forceinline__ void block_reduce(Lane& ln) {
   }
 }
 
-// Scan of one item into a lane-partial; returns in lane 0 the item's
-// (S, sum (j+1) x_j with j local to the item, X folded to element width, NF).
-template <uint32_t DT, class Cfg>
-__device__ __forceinline__ void scan_item(const PlanItem& it, Lane& ln) {
-  constexpr uint32_t es = (DT == SDC_F32) ? 4u : 2u;
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(it.addr);
+// Head, aligned body and tail of an item of ES-byte elements.
+struct Span {
+  const unsigned char* base;
+  uint32_t h, nvec, tail0, ntail;
+};
+
+template <uint32_t ES>
+__device__ __forceinline__ Span span_of(const PlanItem& it) {
+  Span sp;
+  sp.base = reinterpret_cast<const unsigned char*>(it.addr);
   const uint32_t len = it.len;
   const uint32_t mis = (uint32_t)(it.addr & 15u);
-  const uint32_t h = mis ? min(len, (16u - mis) / es) : 0u;
-  const uint32_t nvec = (uint32_t)(((uint64_t)(len - h) * es) / kVecBytes);
-  const uint32_t tail0 = h + nvec * (kVecBytes / es);
-  const uint32_t ntail = len - tail0;
+  sp.h = mis ? min(len, (16u - mis) / ES) : 0u;
+  sp.nvec = (uint32_t)(((uint64_t)(len - sp.h) * ES) / kVecBytes);
+  sp.tail0 = sp.h + sp.nvec * (kVecBytes / ES);
+  sp.ntail = len - sp.tail0;
+  return sp;
+}
+
+// Scan of one item by a workgroup; lane 0 ends with the item's
+// (S, sum (j+1) x_j with j local to the item, X, NF).
+template <class Ty, class Cfg>
+__device__ __forceinline__ void scan_item(const PlanItem& it, Lane& ln) {
+  constexpr uint32_t es = Ty::ES;
+  const Span sp = span_of<es>(it);
+  const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
   const uint32_t t = threadIdx.x;
-  if (t < h) scan_scalar<DT>(base + (uint64_t)t * es, t, ln);
-  if (t >= 128u && t - 128u < ntail) {
-    const uint32_t j = tail0 + (t - 128u);
-    scan_scalar<DT>(base + (uint64_t)j * es, j, ln);
+  if (t < sp.h) scan_scalar<Ty>(sp.base + (uint64_t)t * es, t, rule, ln);
+  if (t >= 128u && t - 128u < sp.ntail) {
+    const uint32_t j = sp.tail0 + (t - 128u);
+    scan_scalar<Ty>(sp.base + (uint64_t)j * es, j, rule, ln);
   }
-  if (nvec) scan_body<DT, Cfg>(base + (uint64_t)h * es, nvec, h, ln);
+  if (sp.nvec) scan_body<Ty, Cfg>(sp.base + (uint64_t)sp.h * es, sp.nvec, sp.h, rule, ln);
   block_reduce(ln);
-  if constexpr (es == 2) ln.x = (ln.x & 0xFFFFu) ^ (ln.x >> 16);
+  ln.x = finish_xor<Ty>(ln.x);
 }
 
 template <class Cfg>
@@ -336,11 +586,7 @@ __global__ void __launch_bounds__(kBlock) fingerprint_kernel(const PlanItem* __r
                                                              sdc_row* __restrict__ out) {
   const PlanItem it = items[blockIdx.x];
   Lane ln;
-  switch (it.dtype_flags & kItemDtypeMask) {
-    case SDC_F32: scan_item<SDC_F32, Cfg>(it, ln); break;
-    case SDC_BF16: scan_item<SDC_BF16, Cfg>(it, ln); break;
-    default: scan_item<SDC_F16, Cfg>(it, ln); break;
-  }
+  dispatch_type(it.dtype_flags, [&](auto ty) { scan_item<decltype(ty), Cfg>(it, ln); });
   if (threadIdx.x != 0) return;
   const uint64_t S = ln.s;
   const uint64_t W = ln.w + it.start * S;
@@ -350,59 +596,53 @@ __global__ void __launch_bounds__(kBlock) fingerprint_kernel(const PlanItem* __r
   sdc_row* dst = (it.dtype_flags & kItemWhole) ? out + it.row : partials + it.slot;
   ulonglong2* d = reinterpret_cast<ulonglong2*>(dst);
   d[0] = ulonglong2{S, W};
-  d[1] = ulonglong2{(unsigned long long)ln.x, ln.nf};
+  d[1] = ulonglong2{ln.x, ln.nf};
 }
 
 // ---- wave items: small tensors, one wave each ---------------------------------
 // The aligned body has at most 64 x kWaveVecs vectors; lane l loads vectors
 // 64*u + l for u = 0 .. kWaveVecs-1 all at once (T = kWaveVecs, missing
 // vectors count as zero), then W_lane = (h+1+E*l)*A + 64*E*(T*A - Q) + C.
-template <uint32_t DT>
+template <class Ty>
 __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane& ln) {
-  typedef typename AccOf<DT>::type Acc;
-  constexpr uint32_t es = (DT == SDC_F32) ? 4u : 2u;
+  typedef Acc<Ty::ES, Ty::SIGNED, Ty::CHK> A_t;
+  constexpr uint32_t es = Ty::ES;
   constexpr uint32_t E = kVecBytes / es;
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(it.addr);
-  const uint32_t len = it.len;
-  const uint32_t mis = (uint32_t)(it.addr & 15u);
-  const uint32_t h = mis ? min(len, (16u - mis) / es) : 0u;
-  const uint32_t nvec = (uint32_t)(((uint64_t)(len - h) * es) / kVecBytes);
-  const uint32_t tail0 = h + nvec * E;
-  const uint32_t ntail = len - tail0;
-  if (l < h) scan_scalar<DT>(base + (uint64_t)l * es, l, ln);
-  if (l >= 32u && l - 32u < ntail) {
-    const uint32_t j = tail0 + (l - 32u);
-    scan_scalar<DT>(base + (uint64_t)j * es, j, ln);
+  const Span sp = span_of<es>(it);
+  const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
+  if (l < sp.h) scan_scalar<Ty>(sp.base + (uint64_t)l * es, l, rule, ln);
+  if (l >= 32u && l - 32u < sp.ntail) {
+    const uint32_t j = sp.tail0 + (l - 32u);
+    scan_scalar<Ty>(sp.base + (uint64_t)j * es, j, rule, ln);
   }
-  if (nvec) {
-    const unsigned char* body = base + (uint64_t)h * es;
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(body, nvec * kVecBytes);
+  if (sp.nvec) {
+    const unsigned char* body = sp.base + (uint64_t)sp.h * es;
+    __amdgpu_buffer_rsrc_t rs = make_rsrc(body, sp.nvec * kVecBytes);
     u32x4 v[kWaveVecs];
 #pragma unroll
     for (uint32_t u = 0; u < kWaveVecs; ++u) {
       const uint32_t vi = u * 64u + l;
-      v[u] = (vi < nvec) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = (vi < sp.nvec) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
     }
-    Acc acc;
+    A_t acc(rule);
 #pragma unroll
     for (uint32_t u = 0; u < kWaveVecs; ++u) acc.add(v[u]);
     const uint64_t T = kWaveVecs;
     const uint64_t A = acc.sum();
     ln.s += A;
-    ln.w += (uint64_t)(h + 1u + E * l) * A + (uint64_t)(64u * E) * (T * A - acc.q) + acc.csum();
+    ln.w += (uint64_t)(sp.h + 1u + E * l) * A + (uint64_t)(64u * E) * (T * A - acc.q) + acc.csum();
     ln.x ^= acc.x;
-    if (acc.flagged()) {  // rare: reload this lane's vectors and count exactly
+    if (acc.chk.flagged()) {  // rare: reload this lane's vectors and count exactly
       uint32_t c = 0;
-      for (uint32_t vi = l; vi < nvec; vi += 64u) c += nonfinite_vec<DT>(load16(rs, vi * kVecBytes));
+      for (uint32_t vi = l; vi < sp.nvec; vi += 64u) c += nf_vec<es>(load16(rs, vi * kVecBytes), rule);
       ln.nf += c;
     }
   }
   wave_reduce(ln);
-  if constexpr (es == 2) ln.x = (ln.x & 0xFFFFu) ^ (ln.x >> 16);
+  ln.x = finish_xor<Ty>(ln.x);
 }
 
-__global__ void __launch_bounds__(kBlock)
-fingerprint_small_kernel(const PlanItem* __restrict__ items,
+__global__ void __launch_bounds__(kBlock) fingerprint_small_kernel(const PlanItem* __restrict__ items,
                                                                    uint32_t n,
                                                                    sdc_row* __restrict__ out) {
   const uint32_t i = wave_item_index();
@@ -410,15 +650,11 @@ fingerprint_small_kernel(const PlanItem* __restrict__ items,
   const PlanItem it = items[i];
   const uint32_t l = threadIdx.x & 63u;
   Lane ln;
-  switch (it.dtype_flags & kItemDtypeMask) {
-    case SDC_F32: scan_small<SDC_F32>(it, l, ln); break;
-    case SDC_BF16: scan_small<SDC_BF16>(it, l, ln); break;
-    default: scan_small<SDC_F16>(it, l, ln); break;
-  }
+  dispatch_type(it.dtype_flags, [&](auto ty) { scan_small<decltype(ty)>(it, l, ln); });
   if (l != 0) return;
   ulonglong2* d = reinterpret_cast<ulonglong2*>(out + it.row);
   d[0] = ulonglong2{ln.s, ln.w};
-  d[1] = ulonglong2{(unsigned long long)ln.x, ln.nf};
+  d[1] = ulonglong2{ln.x, ln.nf};
 }
 
 // Row of each split tensor from its items' partial rows: sums of S and of the
@@ -439,47 +675,34 @@ __global__ void __launch_bounds__(kBlock) merge_rows_kernel(const PlanSplit* __r
     const ulonglong2 a = p[0], b = p[1];
     ln.s += a.x;
     ln.w += a.y;
-    ln.x ^= (uint32_t)b.x;
+    ln.x ^= b.x;
     ln.nf += b.y;
   }
   wave_reduce(ln);
   if (l != 0) return;
   ulonglong2* d = reinterpret_cast<ulonglong2*>(out + sp.row);
   d[0] = ulonglong2{ln.s, ln.w};
-  d[1] = ulonglong2{(unsigned long long)ln.x, ln.nf};
+  d[1] = ulonglong2{ln.x, ln.nf};
 }
 
-// ---- NaN/Inf count only ----------------------------------------------------
-template <uint32_t DT>
+// ---- NaN/Inf count only ----------------------------------------------------------
+template <class Ty>
 __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
-  constexpr uint32_t es = (DT == SDC_F32) ? 4u : 2u;
+  constexpr uint32_t es = Ty::ES;
   constexpr uint32_t kRound = kBlock * kUnroll;
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(it.addr);
-  const uint32_t len = it.len;
-  const uint32_t mis = (uint32_t)(it.addr & 15u);
-  const uint32_t h = mis ? min(len, (16u - mis) / es) : 0u;
-  const uint32_t nvec = (uint32_t)(((uint64_t)(len - h) * es) / kVecBytes);
-  const uint32_t tail0 = h + nvec * (kVecBytes / es);
-  const uint32_t ntail = len - tail0;
   const uint32_t t = threadIdx.x;
   uint32_t c = 0;
-  if (t < h) {
-    const unsigned char* p = base + (uint64_t)t * es;
-    c += nonfinite_bits<DT>(es == 4 ? *reinterpret_cast<const uint32_t*>(p)
-                                    : *reinterpret_cast<const unsigned short*>(p));
-  }
-  if (t >= 128u && t - 128u < ntail) {
-    const unsigned char* p = base + (uint64_t)(tail0 + t - 128u) * es;
-    c += nonfinite_bits<DT>(es == 4 ? *reinterpret_cast<const uint32_t*>(p)
-                                    : *reinterpret_cast<const unsigned short*>(p));
-  }
-  if (nvec) {
-    const unsigned char* body = base + (uint64_t)h * es;
-    bool flag = false;
-    if constexpr (DT == SDC_F32) {
-      float nf = 0.0f;
-      for (uint32_t v0 = 0; v0 < nvec; v0 += kRound) {
-        const uint32_t left = min(nvec - v0, kRound);
+  if constexpr (Ty::CHK != kChkNone) {  // raw integers are never NaN/Inf: nothing to read
+    const Span sp = span_of<es>(it);
+    const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
+    if (t < sp.h) c += nf_exact(load_elem<es>(sp.base + (uint64_t)t * es), rule);
+    if (t >= 128u && t - 128u < sp.ntail)
+      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + t - 128u) * es), rule);
+    if (sp.nvec) {
+      const unsigned char* body = sp.base + (uint64_t)sp.h * es;
+      Chk<Ty::CHK> chk(rule);
+      for (uint32_t v0 = 0; v0 < sp.nvec; v0 += kRound) {
+        const uint32_t left = min(sp.nvec - v0, kRound);
         __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, left * kVecBytes);
         u32x4 v[kUnroll];
 #pragma unroll
@@ -488,40 +711,13 @@ __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
           v[u] = (vi < left) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          nf = __builtin_fmaf(__uint_as_float(v[u].x), 0.0f, nf);
-          nf = __builtin_fmaf(__uint_as_float(v[u].y), 0.0f, nf);
-          nf = __builtin_fmaf(__uint_as_float(v[u].z), 0.0f, nf);
-          nf = __builtin_fmaf(__uint_as_float(v[u].w), 0.0f, nf);
-        }
+        for (int u = 0; u < kUnroll; ++u) chk.add(v[u]);
       }
-      flag = __float_as_uint(nf) != 0u;
-    } else {
-      h2 nf = {0, 0};
-      const h2 z = {0, 0};
-      for (uint32_t v0 = 0; v0 < nvec; v0 += kRound) {
-        const uint32_t left = min(nvec - v0, kRound);
-        __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, left * kVecBytes);
-        u32x4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const uint32_t vi = u * kBlock + t;
-          v[u] = (vi < left) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
+      if (chk.flagged()) {
+        for (uint32_t vi = t; vi < sp.nvec; vi += kBlock) {
+          __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
+          c += nf_vec<es>(load16(rs, 0), rule);
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          nf = __builtin_elementwise_fma(as_h2(v[u].x), z, nf);
-          nf = __builtin_elementwise_fma(as_h2(v[u].y), z, nf);
-          nf = __builtin_elementwise_fma(as_h2(v[u].z), z, nf);
-          nf = __builtin_elementwise_fma(as_h2(v[u].w), z, nf);
-        }
-      }
-      flag = h2_bits(nf) != 0u;
-    }
-    if (flag) {
-      for (uint32_t vi = t; vi < nvec; vi += kBlock) {
-        __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
-        c += nonfinite_vec<DT>(load16(rs, 0));
       }
     }
   }
@@ -536,17 +732,20 @@ __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
   return c;
 }
 
+// Signedness does not change the NaN/Inf count; it is dropped here.
+template <class Ty>
+struct Unsigned {
+  typedef TypeTag<Ty::ES, false, Ty::CHK> type;
+};
+
 __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __restrict__ items,
                                                            sdc_row* __restrict__ partials,
                                                            uint64_t* __restrict__ counts,
                                                            uint64_t* __restrict__ total) {
   const PlanItem it = items[blockIdx.x];
-  uint32_t c;
-  switch (it.dtype_flags & kItemDtypeMask) {
-    case SDC_F32: c = nonfinite_item<SDC_F32>(it); break;
-    case SDC_BF16: c = nonfinite_item<SDC_BF16>(it); break;
-    default: c = nonfinite_item<SDC_F16>(it); break;
-  }
+  uint32_t c = 0;
+  dispatch_type(it.dtype_flags & ~kItemSigned,
+                [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type>(it); });
   if (threadIdx.x != 0) return;
   if (counts) {
     if (it.dtype_flags & kItemWhole) counts[it.row] = c;
@@ -556,32 +755,23 @@ __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __res
   if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
 }
 
-template <uint32_t DT>
+template <class Ty>
 __device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t l) {
-  constexpr uint32_t es = (DT == SDC_F32) ? 4u : 2u;
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(it.addr);
-  const uint32_t len = it.len;
-  const uint32_t mis = (uint32_t)(it.addr & 15u);
-  const uint32_t h = mis ? min(len, (16u - mis) / es) : 0u;
-  const uint32_t nvec = (uint32_t)(((uint64_t)(len - h) * es) / kVecBytes);
-  const uint32_t tail0 = h + nvec * (kVecBytes / es);
-  const uint32_t ntail = len - tail0;
+  constexpr uint32_t es = Ty::ES;
   uint32_t c = 0;
-  auto scalar = [&](uint32_t j) {
-    const unsigned char* p = base + (uint64_t)j * es;
-    uint32_t x;
-    if constexpr (DT == SDC_F32) x = *reinterpret_cast<const uint32_t*>(p);
-    else x = *reinterpret_cast<const unsigned short*>(p);
-    c += nonfinite_bits<DT>(x);
-  };
-  if (l < h) scalar(l);
-  if (l >= 32u && l - 32u < ntail) scalar(tail0 + (l - 32u));
-  if (nvec) {
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (uint64_t)h * es, nvec * kVecBytes);
+  if constexpr (Ty::CHK != kChkNone) {
+    const Span sp = span_of<es>(it);
+    const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
+    if (l < sp.h) c += nf_exact(load_elem<es>(sp.base + (uint64_t)l * es), rule);
+    if (l >= 32u && l - 32u < sp.ntail)
+      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - 32u) * es), rule);
+    if (sp.nvec) {
+      __amdgpu_buffer_rsrc_t rs = make_rsrc(sp.base + (uint64_t)sp.h * es, sp.nvec * kVecBytes);
 #pragma unroll
-    for (uint32_t u = 0; u < kWaveVecs; ++u) {
-      const uint32_t vi = u * 64u + l;
-      if (vi < nvec) c += nonfinite_vec<DT>(load16(rs, vi * kVecBytes));
+      for (uint32_t u = 0; u < kWaveVecs; ++u) {
+        const uint32_t vi = u * 64u + l;
+        if (vi < sp.nvec) c += nf_vec<es>(load16(rs, vi * kVecBytes), rule);
+      }
     }
   }
 #pragma unroll
@@ -589,8 +779,7 @@ __device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t
   return c;
 }
 
-__global__ void __launch_bounds__(kBlock)
-nonfinite_small_kernel(const PlanItem* __restrict__ items,
+__global__ void __launch_bounds__(kBlock) nonfinite_small_kernel(const PlanItem* __restrict__ items,
                                                                  uint32_t n,
                                                                  uint64_t* __restrict__ counts,
                                                                  uint64_t* __restrict__ total) {
@@ -598,12 +787,9 @@ nonfinite_small_kernel(const PlanItem* __restrict__ items,
   if (i >= n) return;
   const PlanItem it = items[i];
   const uint32_t l = threadIdx.x & 63u;
-  uint32_t c;
-  switch (it.dtype_flags & kItemDtypeMask) {
-    case SDC_F32: c = nonfinite_small<SDC_F32>(it, l); break;
-    case SDC_BF16: c = nonfinite_small<SDC_BF16>(it, l); break;
-    default: c = nonfinite_small<SDC_F16>(it, l); break;
-  }
+  uint32_t c = 0;
+  dispatch_type(it.dtype_flags & ~kItemSigned,
+                [&](auto ty) { c = nonfinite_small<typename Unsigned<decltype(ty)>::type>(it, l); });
   if (l != 0) return;
   if (counts) counts[it.row] = c;
   if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
@@ -672,7 +858,7 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
   if (item_bytes % kVecBytes != 0 || item_bytes > kItemBytesMax) return SDC_ERR_INVALID;
   uint64_t elems = 0, bytes = 0;
   for (uint64_t k = 0; k < n; ++k) {
-    if (t[k].flags != 0) return SDC_ERR_INVALID;
+    if ((t[k].flags & ~(uint32_t)SDC_FLAG_SIGNED) != 0) return SDC_ERR_INVALID;
     const uint32_t es = element_size(t[k].dtype);
     if (es == 0) return SDC_ERR_DTYPE;
     if (!has_data(t[k])) continue;
@@ -748,7 +934,7 @@ void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<uns
       it.len = (uint32_t)len;
       it.row = (uint32_t)k;
       it.slot = whole ? 0u : (uint32_t)slot++;
-      it.dtype_flags = t[k].dtype | whole;
+      it.dtype_flags = t[k].dtype | whole | ((t[k].flags & SDC_FLAG_SIGNED) ? kItemSigned : 0u);
     });
   }
 }

@@ -14,9 +14,10 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 // Bytes of one coalesced vector load per lane.
 constexpr uint32_t kVecBytes = 16;
-// Largest work item.  Bounds the per-lane 32-bit accumulators of the 16-bit
-// path: with U-way unrolling a lane sees at most kItemBytesMax / (16 * 256)
-// = 1024 vectors of 8 elements, so sum_x < 2^29 and sum_(k x) < 2^31.
+// Largest work item.  Bounds the per-lane 32-bit accumulators of the 1- and
+// 2-byte paths: a lane sees at most kItemBytesMax / (16 * 256) = 1024 vectors,
+// so for 16-bit elements |sum x| < 2^29 and |sum k x| < 2^31, for bytes
+// sum x < 2^23 and sum k x < 2^25.
 constexpr uint64_t kItemBytesMax = 4ull << 20;
 // Automatic item size: aim at this many items, within [kAutoMin, kAutoMax].
 constexpr uint64_t kAutoTargetItems = 65536;
@@ -32,8 +33,10 @@ constexpr uint64_t kPlanMagic = 0x31766E6163534453ull;  // "SDScanv1", little-en
 constexpr uint32_t kWaveVecs = 8;
 constexpr uint32_t kWaveBodyVecs = 64 * kWaveVecs;
 
-// Item flag: the item is the whole tensor, so it stores the tensor's row.
+// Item flags: the item is the whole tensor, so it stores the tensor's row;
+// the tensor's 2-/4-byte patterns are sign-extended (SDC_FLAG_SIGNED).
 constexpr uint32_t kItemWhole = 1u << 8;
+constexpr uint32_t kItemSigned = 1u << 9;
 constexpr uint32_t kItemDtypeMask = 0xFFu;
 
 // Device plan, all offsets from the plan's base:
@@ -64,7 +67,7 @@ struct PlanItem {
   uint32_t len;          // elements in the item
   uint32_t row;          // output row (tensor index in the list)
   uint32_t slot;         // partial-row slot (split tensors only)
-  uint32_t dtype_flags;  // SDC_F32 / SDC_BF16 / SDC_F16 | kItemWhole
+  uint32_t dtype_flags;  // SDC_* element type | kItemWhole | kItemSigned
 };
 static_assert(sizeof(PlanItem) == 32, "plan item layout");
 
@@ -92,7 +95,14 @@ inline PlanOffsets plan_offsets(uint64_t n_items, uint64_t n_split, uint64_t n_s
 }
 
 inline uint32_t element_size(uint32_t dtype) {
-  return dtype == SDC_F32 ? 4u : (dtype == SDC_BF16 || dtype == SDC_F16) ? 2u : 0u;
+  switch (dtype) {
+    case SDC_F32: case SDC_U32: return 4;
+    case SDC_BF16: case SDC_F16: case SDC_U16: return 2;
+    case SDC_F64: case SDC_U64: return 8;
+    case SDC_U8: case SDC_FP8_E4M3: case SDC_FP8_E5M2: case SDC_FP8_E4M3FNUZ:
+    case SDC_FP8_E5M2FNUZ: return 1;
+    default: return 0;
+  }
 }
 
 // Thread-local record of the last failing HIP call.

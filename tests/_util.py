@@ -12,7 +12,11 @@ import torch
 
 import oracle as O
 
-CODE = {torch.float32: O.F32, torch.bfloat16: O.BF16, torch.float16: O.F16}
+CODE = {torch.float32: O.F32, torch.bfloat16: O.BF16, torch.float16: O.F16,
+        torch.float64: O.F64, torch.uint8: O.U8, torch.int8: O.U8, torch.bool: O.U8,
+        torch.float8_e4m3fn: O.FP8_E4M3, torch.float8_e5m2: O.FP8_E5M2,
+        torch.float8_e4m3fnuz: O.FP8_E4M3FNUZ, torch.float8_e5m2fnuz: O.FP8_E5M2FNUZ,
+        torch.int16: O.U16, torch.int32: O.U32, torch.int64: O.U64}
 THREADS = int(os.environ.get("SDC_TEST_THREADS", "16"))
 
 
@@ -27,12 +31,12 @@ def host_bytes(t):
     return t.detach().reshape(-1).view(torch.uint8).cpu().numpy()
 
 
-def oracle_rows(tensors, threads=THREADS):
+def oracle_rows(tensors, threads=THREADS, flags=0):
     """uint64 [n, 4] oracle rows of a list of device tensors (None allowed)."""
     def one(t):
         if t is None:
             return (0, 0, 0, 0)
-        return O.fingerprint(host_bytes(t), CODE[t.dtype])
+        return O.fingerprint(host_bytes(t), CODE[t.dtype], flags)
     with ThreadPoolExecutor(max_workers=threads) as ex:
         rows = list(ex.map(one, tensors))
     return np.array(rows, dtype=np.uint64).reshape(-1, 4)

@@ -80,10 +80,11 @@ def test_plan_bytes_host_only():
 
 
 @pytest.mark.parametrize("desc,item_bytes,code", [
-    ((0x10000, 10, 7, 0), 0, -2),      # unknown dtype
+    ((0x10000, 10, 99, 0), 0, -2),     # unknown dtype
+    ((0x10001, 10, 3, 0), 0, -3),      # fp64 pointer not 8-byte aligned
     ((0x10001, 10, 0, 0), 0, -3),      # fp32 pointer not 4-byte aligned
     ((0x10001, 10, 1, 0), 0, -3),      # bf16 pointer odd
-    ((0x10000, 10, 0, 1), 0, -1),      # flags must be 0
+    ((0x10000, 10, 0, 2), 0, -1),      # only SDC_FLAG_SIGNED is a flag
     ((0x10000, 10, 0, 0), 24, -1),     # item size not a multiple of 16
     ((0x10000, 10, 0, 0), 8 << 20, -1),  # item size above 4 MiB
     ((0x10000, 1 << 62, 0, 0), 0, -7),  # too many elements

@@ -34,7 +34,8 @@ def random_bits(nbytes, seed):
 
 
 def carve(buf, offset, n, dtype):
-    return buf[offset:offset + n * ES[dtype]].view(dtype)
+    es = torch.empty(0, dtype=dtype).element_size()
+    return buf[offset:offset + n * es].view(dtype)
 
 
 def scan(tensors, item_bytes=0):
@@ -233,3 +234,68 @@ def test_diff_matches_oracle():
                 assert got["n_diff"] == ref["n_diff"]
                 assert got["indices"] == ref["indices"]
                 assert got["hints"] == ref["hints"]
+
+
+# ---------------------------------------------------------------------------
+# every element type, zero- and sign-extended
+# ---------------------------------------------------------------------------
+ALL_TYPES = [torch.float32, torch.bfloat16, torch.float16, torch.float64, torch.uint8, torch.int8,
+             torch.float8_e4m3fn, torch.float8_e5m2, torch.float8_e4m3fnuz, torch.float8_e5m2fnuz,
+             torch.int16, torch.int32, torch.int64]
+TYPE_SIZES = [1, 2, 3, 7, 15, 16, 17, 33, 255, 511, 513, 4095, 4097, 8191, 8193, 65537, 1_000_003]
+
+
+@pytest.mark.parametrize("dtype", ALL_TYPES, ids=[str(t).split(".")[1] for t in ALL_TYPES])
+@pytest.mark.parametrize("signed", [False, True])
+def test_all_types_sizes_offsets(dtype, signed):
+    es = torch.empty(0, dtype=dtype).element_size()
+    flags = O.SIGNED if signed else 0
+    for n in TYPE_SIZES:
+        buf = random_bits(n * es + 16, seed=1000 + n)
+        tensors = [carve(buf, off, n, dtype) for off in range(0, 16, es)]
+        say(f"case types dtype={dtype} signed={signed} n={n}")
+        plan = sdc.sdc_plan_build(tensors, signed=signed)
+        out = sdc.sdc_fingerprint_plan(plan)
+        counts, total = sdc.sdc_nonfinite(plan)
+        torch.cuda.synchronize()
+        ref = oracle_rows(tensors, flags=flags)
+        assert_rows_equal(sdc.rows_numpy(out), ref)
+        assert counts.cpu().numpy().astype(np.uint64).tolist() == ref[:, 3].tolist()
+        assert int(total.item()) == int(ref[:, 3].sum())
+
+
+def test_all_types_item_sizes_and_mixed_lists():
+    rng = np.random.default_rng(99)
+    tensors = []
+    for k in range(3000):
+        dt = ALL_TYPES[int(rng.integers(0, len(ALL_TYPES)))]
+        es = torch.empty(0, dtype=dt).element_size()
+        n = int(np.exp(rng.uniform(0, np.log(300_000))))
+        off = es * int(rng.integers(0, 16 // es))
+        tensors.append(carve(random_bits(n * es + 16, seed=5000 + k), off, n, dt))
+    for signed in (False, True):
+        ref = oracle_rows(tensors, flags=O.SIGNED if signed else 0)
+        for ib in (0, 768, 4096, 1 << 20):
+            say(f"case mixed types signed={signed} item_bytes={ib}")
+            plan = sdc.sdc_plan_build(tensors, item_bytes=ib, signed=signed)
+            out = sdc.sdc_fingerprint_plan(plan)
+            torch.cuda.synchronize()
+            assert_rows_equal(sdc.rows_numpy(out), ref)
+
+
+def test_fp8_and_fp64_special_patterns():
+    # every fp8 pattern repeated, and fp64 NaN/Inf at head, body and tail
+    b = torch.arange(256, dtype=torch.int16, device=DEV).to(torch.uint8).repeat(1000)
+    tensors = [b.view(t) for t in (torch.float8_e4m3fn, torch.float8_e5m2,
+                                   torch.float8_e4m3fnuz, torch.float8_e5m2fnuz, torch.uint8)]
+    d = torch.empty(100_001, dtype=torch.float64, device=DEV).normal_(generator=gen(8))
+    iv = d.view(torch.int64)
+    iv[0] = 0x7FF0000000000000
+    iv[50_000] = -0x0008000000000000  # 0xFFF8..., a negative quiet NaN
+    iv[-1] = 0x7FF0000000000001
+    tensors.append(d)
+    say("case fp8/fp64 specials")
+    rows, plan = scan(tensors)
+    ref = oracle_rows(tensors)
+    assert_rows_equal(rows, ref)
+    assert rows[:, 3].tolist() == [2000, 8000, 1000, 1000, 0, 3]

@@ -11,7 +11,7 @@ import pytest
 
 import silent_corruption_detection_amd as sdc
 
-ES = {0: 4, 1: 2, 2: 2}
+ES = {0: 4, 1: 2, 2: 2, 3: 8, 4: 1, 5: 1, 6: 1, 7: 1, 8: 1, 9: 2, 10: 4, 11: 8}
 WHOLE = 0x100
 WAVE_BODY_VECS = 512
 ITEM_MAX = 4 << 20
@@ -75,6 +75,7 @@ def check_plan(descs, item_bytes):
             assert int(x["start"]) == pos, (k, pos, x)
             assert int(x["addr"]) == ptr + pos * es
             assert int(x["df"]) & 0xFF == dt
+            assert bool(int(x["df"]) & 0x200) == bool(descs[k][3] & 1)
             ln = int(x["len"])
             assert ln > 0
             if pos > 0:
@@ -117,7 +118,7 @@ def test_random_lists_are_covered_exactly(item_bytes):
     base = 0x7F0000000000
     descs = []
     for k in range(300):
-        dt = int(rng.integers(0, 3))
+        dt = int(rng.integers(0, 12))
         es = ES[dt]
         r = rng.random()
         if r < 0.05:
@@ -127,7 +128,7 @@ def test_random_lists_are_covered_exactly(item_bytes):
         if item_bytes == 16:
             numel = min(numel, 20000)  # keep the item list small
         ptr = base + int(rng.integers(0, 1 << 20)) * 16 + int(rng.integers(0, 16 // es)) * es
-        descs.append((ptr, numel, dt, 0))
+        descs.append((ptr, numel, dt, int(rng.integers(0, 2))))
     info = check_plan(descs, item_bytes)
     assert info.n_items > 0
 
