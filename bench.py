@@ -132,7 +132,7 @@ def bench_c2(args, torch, sdc, W_):
 def bench_other(args, torch, sdc, W_, name):
     """Timing of the other workloads (c1 replicas, c3 gradients + replay, c4
     small tensors): scan + the comparison each is for, and for c3 the
-    NaN/Inf-count launch on its own."""
+    NaN/Inf-count and squared-norm launches on their own."""
     w = W_.BUILDERS[name]("cuda")
     plan = sdc.sdc_plan_build(w.tensors)
     stream = torch.cuda.current_stream()
@@ -170,6 +170,20 @@ def bench_other(args, torch, sdc, W_, name):
         res.update(nonfinite_kernel_ms=round(nkms, 4),
                    nonfinite_gbs=round(plan.total_bytes / nkms / 1e6, 1),
                    nonfinite_total=int(total.item()))
+        sq = torch.empty(max(plan.n_tensors, 1), dtype=torch.float64, device="cuda")
+        sq_total = torch.empty(1, dtype=torch.float64, device="cuda")
+        flag = torch.empty(1, dtype=torch.int32, device="cuda")
+
+        def sq_step(ev):
+            if ev is not None:
+                ev[0].record(stream)
+            sdc.sdc_sqnorm(plan, sq, sq_total, flag, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        _, skms = time_steps(sq_step, args.steps, args.warmup, stream)
+        res.update(sqnorm_ms=round(skms, 4), sqnorm_gbs=round(plan.total_bytes / skms / 1e6, 1),
+                   sqnorm_frac_of_hbm_peak=round(plan.total_bytes / skms / 1e6 / HBM_PEAK_GBS, 4),
+                   sqnorm_flag=int(flag.item()))
     return res
 
 

@@ -192,6 +192,19 @@ int32_t sdc_fingerprint_plan(const void* d_plan, const sdc_plan_info* h_info, sd
 int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info, uint64_t* d_counts,
                       uint64_t* d_total, sdc_stream_t stream);
 
+/* [BLOG] "Check 1", the norm-based form: d_sq[k] = sum of the squared values
+ * of tensor k's elements (n_tensors doubles), *d_total = their sum, and
+ * *d_flag (may be NULL) = 1 when *d_total rounded to fp32 is not finite --
+ * exactly when an fp32 norm of these tensors would be NaN or Inf: any NaN or
+ * Inf element, or a finite norm above ~1.8e19.  Values are decoded exactly
+ * from each floating-point type (raw integer types contribute 0) and summed
+ * in double in an order fixed by the plan, so results are bit-reproducible
+ * for a given plan (a different item size may change the last bits).
+ * ASYNCHRONOUS.  Uses the plan's scratch rows, like a scan.  Errors as
+ * sdc_fingerprint_plan. */
+int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, double* d_sq,
+                   double* d_total, uint32_t* d_flag, sdc_stream_t stream);
+
 /* One-shot form of sdc_plan_build + sdc_fingerprint_plan: d_ws is a device
  * workspace of at least sdc_plan_bytes(h_tensors, n, 0) bytes that holds the
  * plan.  The plan upload is synchronous; the scan is asynchronous on stream.

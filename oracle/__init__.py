@@ -64,6 +64,12 @@ def lib():
         L.oracle_majority_compare.argtypes = [P, U32, U64, U32, P, P, P]
         L.oracle_flip_hint.argtypes = [P, P, P]
         L.oracle_fingerprint_diff.argtypes = [P, P, U64, U32, P, P, U64, P]
+        L.oracle_value.argtypes = [U64, U32]
+        L.oracle_value.restype = ctypes.c_double
+        L.oracle_sqnorm.argtypes = [P, U64, U32, P]
+        L.oracle_sqnorm.restype = ctypes.c_int
+        L.oracle_sqnorm_flag.argtypes = [ctypes.c_double]
+        L.oracle_sqnorm_flag.restype = ctypes.c_int
         L.oracle_ring_pairs.argtypes = [P, U32, U64, U32, P]
         L.oracle_ring_localize.argtypes = [P, U32, U32, P, P]
         L.oracle_confirm_verdict.argtypes = [P, P, P, P, U64, P]
@@ -222,3 +228,22 @@ def confirm_verdict(third, self_, orig, peer):
     _check(lib().oracle_confirm_verdict(*[a.ctypes.data if width else None for a in arrs], width,
                                         ctypes.byref(v)))
     return v.value
+
+
+def value(x, dtype):
+    return lib().oracle_value(int(x), dtype)
+
+
+def sqnorm(data, dtype):
+    """sum of squared element values (double, index order) of a host array."""
+    out = ctypes.c_double(0.0)
+    if data is None:
+        _check(lib().oracle_sqnorm(None, 0, dtype, ctypes.byref(out)))
+    else:
+        arr, ptr = _host_bytes(data)
+        _check(lib().oracle_sqnorm(ptr, arr.nbytes // ESIZE[dtype], dtype, ctypes.byref(out)))
+    return out.value
+
+
+def sqnorm_flag(sq):
+    return bool(lib().oracle_sqnorm_flag(float(sq)))

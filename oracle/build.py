@@ -14,7 +14,7 @@ def build(verbose: bool = False) -> str:
     src = os.path.join(HERE, "sdc_oracle.c")
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-           "-Wall", "-Wextra", "-Werror", "-o", tmp, src]
+           "-Wall", "-Wextra", "-Werror", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

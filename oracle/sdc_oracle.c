@@ -9,6 +9,7 @@
  */
 #include "sdc_oracle.h"
 
+#include <math.h>
 #include <stddef.h>
 #include <string.h>
 
@@ -310,4 +311,67 @@ int oracle_confirm_verdict(const uint64_t* third, const uint64_t* self, const ui
     *verdict = ORACLE_VERDICT_UNATTRIBUTABLE;
   }
   return ORACLE_OK;
+}
+
+/* Decoding from the formats' definitions: (-1)^s * 2^(e - bias) * (1 + f)
+ * for normal numbers, (-1)^s * 2^(1 - bias) * f for subnormals (e == 0),
+ * with f the mantissa field over 2^(mantissa bits). */
+static double decode(uint64_t x, int ebits, int mbits, int bias) {
+  uint64_t m = x & ((1ull << mbits) - 1u);
+  uint64_t e = (x >> mbits) & ((1ull << ebits) - 1u);
+  int s = (int)((x >> (ebits + mbits)) & 1u);
+  double f = (double)m / (double)(1ull << mbits);
+  double v = (e == 0) ? ldexp(f, 1 - bias) : ldexp(1.0 + f, (int)e - bias);
+  return s ? -v : v;
+}
+
+double oracle_value(uint64_t x, uint32_t dtype) {
+  switch (dtype) {
+    case ORACLE_F32: case ORACLE_BF16: case ORACLE_F16: case ORACLE_F64: case ORACLE_FP8_E5M2:
+      if (oracle_is_nonfinite(x, dtype)) {  /* IEEE: mantissa 0 is Inf, else NaN */
+        int mbits = dtype == ORACLE_F32 ? 23 : dtype == ORACLE_BF16 ? 7 : dtype == ORACLE_F16 ? 10
+                  : dtype == ORACLE_F64 ? 52 : 2;
+        int sbit = dtype == ORACLE_F32 ? 31 : dtype == ORACLE_F64 ? 63 : dtype == ORACLE_FP8_E5M2 ? 7 : 15;
+        if ((x & ((1ull << mbits) - 1u)) != 0) return NAN;
+        return ((x >> sbit) & 1u) ? -INFINITY : INFINITY;
+      }
+      break;
+    case ORACLE_FP8_E4M3: case ORACLE_FP8_E4M3FNUZ: case ORACLE_FP8_E5M2FNUZ:
+      if (oracle_is_nonfinite(x, dtype)) return NAN;  /* these formats have no Inf */
+      break;
+    default:
+      return 0.0;
+  }
+  switch (dtype) {
+    case ORACLE_F32: return decode(x, 8, 23, 127);
+    case ORACLE_BF16: return decode(x, 8, 7, 127);
+    case ORACLE_F16: return decode(x, 5, 10, 15);
+    case ORACLE_F64: return decode(x, 11, 52, 1023);
+    case ORACLE_FP8_E5M2: return decode(x, 5, 2, 15);
+    case ORACLE_FP8_E4M3: return decode(x, 4, 3, 7);
+    case ORACLE_FP8_E4M3FNUZ: return decode(x, 4, 3, 8);
+    case ORACLE_FP8_E5M2FNUZ: return decode(x, 5, 2, 16);
+    default: return 0.0;
+  }
+}
+
+int oracle_sqnorm(const void* data, uint64_t numel, uint32_t dtype, double* out) {
+  if (out == NULL) return ORACLE_EINVAL;
+  uint32_t esize = oracle_element_size(dtype);
+  if (esize == 0) return ORACLE_EDTYPE;
+  double acc = 0.0;
+  if (data != NULL) {
+    const unsigned char* base = (const unsigned char*)data;
+    for (uint64_t i = 0; i < numel; ++i) {
+      double v = oracle_value(load_bits(base, i, esize), dtype);
+      acc += v * v;
+    }
+  }
+  *out = acc;
+  return ORACLE_OK;
+}
+
+int oracle_sqnorm_flag(double sq) {
+  float f = (float)sq;
+  return !isfinite(f);
 }

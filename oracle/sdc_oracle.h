@@ -125,6 +125,21 @@ int oracle_fingerprint_diff(const oracle_row* a, const oracle_row* b, uint64_t T
                             uint32_t col_mask, uint64_t* n_diff, uint64_t* idx, uint64_t cap,
                             oracle_hint* hints);
 
+/* ---- squared norm ("Check 1: NaN/Inf gradients, ..."): the local gradient
+ * norm is flagged when it is NaN or Inf in fp32 (which also catches finite
+ * overflow of the squared sum). ------------------------------------------- */
+
+/* Value of one element as a double, decoded from its type's bit layout
+ * (raw integer types: 0, they carry no floating-point value). */
+double oracle_value(uint64_t x, uint32_t dtype);
+
+/* sum_i value_i^2 of one tensor, summed in index order in double. */
+int oracle_sqnorm(const void* data, uint64_t numel, uint32_t dtype, double* out);
+
+/* 1 when the squared sum, rounded to fp32, is not finite (NaN, Inf, or a
+ * norm too large for fp32), else 0. */
+int oracle_sqnorm_flag(double sq);
+
 /* ---- ring replay audit ("Check 2: Ring replay, before the optimizer step") --
  * table: n ranks x 2 results x width uint64 words, rank-major.  Result 0 of
  * rank r is r's own result (loss bits and gradient fingerprints), result 1 is

@@ -20,7 +20,7 @@ __all__ = [
     "sdc_nonfinite", "sdc_fingerprint", "sdc_majority_ws_bytes", "sdc_majority_compare",
     "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
     "sdc_abi_version", "rows_numpy", "LIB_PATH", "sdc_ring_ws_bytes", "sdc_ring_compare",
-    "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS",
+    "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS", "sdc_sqnorm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
@@ -79,6 +79,7 @@ def _load():
         "sdc_diff_ws_bytes": [U64, U64, P],
         "sdc_fingerprint_diff": [P, P, U64, U32, P, U64, P, P, U64, P, P],
         "sdc_plan_pack_host": [P, U64, U64, P, U64, P],
+        "sdc_sqnorm": [P, P, P, P, P, P],
         "sdc_ring_ws_bytes": [U32, P],
         "sdc_ring_compare": [P, U32, U64, U32, P, U64, P, P],
         "sdc_ring_localize": [P, U32, U32, P, P],
@@ -380,3 +381,21 @@ def sdc_confirm_verdict(third, self_, orig, peer, stream=None):
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.byref(out),
                                     _stream_handle(stream, third.device)), "sdc_confirm_verdict")
     return out.value
+
+
+def sdc_sqnorm(plan, sq=None, total=None, flag=None, stream=None):
+    """Per-tensor squared norms (float64 device tensor), their total and the
+    norm-check flag (int32 device tensor: 1 = the fp32 norm is not finite).
+    Asynchronous."""
+    dev = plan.device
+    if sq is None:
+        sq = torch.empty(max(plan.n_tensors, 1), dtype=torch.float64, device=dev)
+    if total is None:
+        total = torch.empty(1, dtype=torch.float64, device=dev)
+    if flag is None:
+        flag = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(_lib.sdc_sqnorm(ctypes.c_void_p(plan.buf.data_ptr()), ctypes.byref(plan.info),
+                           ctypes.c_void_p(sq.data_ptr()), ctypes.c_void_p(total.data_ptr()),
+                           ctypes.c_void_p(flag.data_ptr()), _stream_handle(stream, dev)),
+           "sdc_sqnorm")
+    return sq[:plan.n_tensors], total, flag

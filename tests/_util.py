@@ -52,6 +52,24 @@ def oracle_nonfinite(tensors, threads=THREADS):
         return np.array(list(ex.map(one, tensors)), dtype=np.uint64)
 
 
+def oracle_sqnorms(tensors, threads=THREADS):
+    def one(t):
+        return 0.0 if t is None else O.sqnorm(host_bytes(t), CODE[t.dtype])
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(one, tensors))
+
+
+def assert_sq_close(gpu, ref, numels):
+    """Squared sums of non-negative terms: |gpu - ref| <= 2 (n + 1) 2^-53 ref;
+    NaN and Inf must match exactly."""
+    import math
+    for k, (g, r, n) in enumerate(zip(list(gpu), ref, numels)):
+        if math.isfinite(r):
+            assert abs(g - r) <= (2 * n + 2) * 2.0 ** -53 * r, (k, n, g, r)
+        else:
+            assert (math.isnan(g) and math.isnan(r)) or g == r, (k, n, g, r)
+
+
 def assert_rows_equal(gpu, ref, names=None):
     gpu = np.asarray(gpu, dtype=np.uint64).reshape(-1, 4)
     ref = np.asarray(ref, dtype=np.uint64).reshape(-1, 4)

@@ -6,9 +6,11 @@ Expected outcomes come from the generators' own records of what they wrote
 from the oracle, never from the HIP path:
   c1, c2  every row equals the oracle's; the majority compare names exactly
           the corrupted replica.
-  c3      rows and NaN/Inf counts equal the oracle's; the replay differs from
-          the original in exactly the flipped tensor, and the flip hint gives
-          the flipped element and bit.
+  c3      rows, NaN/Inf counts and squared norms equal the oracle's (norms
+          within the summation bound); the norm check flags the list and
+          clears it without the tensors that hold NaN/Inf; the replay differs
+          from the original in exactly the flipped tensor, and the flip hint
+          gives the flipped element and bit.
   c4      rows equal the oracle's for all 300,000 tensors; the named replicas
           are those the corruptions went to.
   c5      (141 GB) rows of a sample of tensors equal the oracle's; a second
@@ -24,7 +26,7 @@ import torch
 import oracle as O
 import silent_corruption_detection_amd as sdc
 import workloads as W
-from _util import assert_rows_equal, oracle_nonfinite, oracle_rows, say
+from _util import assert_rows_equal, assert_sq_close, oracle_nonfinite, oracle_rows, oracle_sqnorms, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -83,6 +85,21 @@ def test_c3_gradients_nonfinite_and_replay():
     assert int(total.item()) == int(ref_nf.sum())
     # every written NaN/Inf is counted in the original
     assert int(ref_nf[:w.T].sum()) == w.meta["n_nonfinite"] == len(w.nonfinite)
+    say("case c3: squared norms")
+    sq, sq_total, flag = sdc.sdc_sqnorm(plan)
+    torch.cuda.synchronize()
+    ref_sq = oracle_sqnorms(w.tensors)
+    assert_sq_close(sq.cpu().tolist(), ref_sq, [t.numel() for t in w.tensors])
+    assert int(flag.item()) == int(len(w.nonfinite) > 0) == 1
+    # the same gradients without their NaN/Inf: a finite norm, flag clear
+    clean_idx = sorted({tk for tk, _, _ in w.nonfinite} ^ set(range(w.T)))
+    clean = sdc.sdc_plan_build([w.tensors[k] for k in clean_idx])
+    sq_c, tot_c, flag_c = sdc.sdc_sqnorm(clean)
+    torch.cuda.synchronize()
+    assert int(flag_c.item()) == 0
+    ref_c = sum(ref_sq[k] for k in clean_idx)
+    n_c = sum(w.tensors[k].numel() for k in clean_idx) + len(clean_idx)
+    assert abs(float(tot_c.item()) - ref_c) <= (2 * n_c + 2) * 2.0 ** -53 * ref_c
     inj = w.injections[0]
     T = w.T
     d = sdc.sdc_fingerprint_diff(out[:T].contiguous(), out[T:].contiguous())
