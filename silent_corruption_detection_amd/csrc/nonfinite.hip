@@ -1,0 +1,175 @@
+// nonfinite.hip -- element-exact NaN/Inf counts per tensor over a scan plan
+// (AWS Machine Learning Blog, "Detecting and recovering from silent data
+// corruption on Amazon SageMaker HyperPod", section "Check 1"), for gfx950.
+//
+// Same items and traversal as the fingerprint scan, but only the fast
+// "may hold NaN/Inf" flag is computed per lane; a lane whose flag is set
+// recounts its own vectors with the type's exact rule.  Raw integer tensors
+// are never read.
+#include "scan_device.h"
+
+namespace sdc {
+namespace {
+
+// ---- NaN/Inf count only ----------------------------------------------------------
+template <class Ty>
+__device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
+  constexpr uint32_t es = Ty::ES;
+  constexpr uint32_t kRound = kBlock * kUnroll;
+  const uint32_t t = threadIdx.x;
+  uint32_t c = 0;
+  if constexpr (Ty::CHK != kChkNone) {  // raw integers are never NaN/Inf: nothing to read
+    const Span sp = span_of<es>(it);
+    const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
+    if (t < sp.h) c += nf_exact(load_elem<es>(sp.base + (uint64_t)t * es), rule);
+    if (t >= 128u && t - 128u < sp.ntail)
+      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + t - 128u) * es), rule);
+    if (sp.nvec) {
+      const unsigned char* body = sp.base + (uint64_t)sp.h * es;
+      Chk<Ty::CHK> chk(rule);
+      for (uint32_t v0 = 0; v0 < sp.nvec; v0 += kRound) {
+        const uint32_t left = min(sp.nvec - v0, kRound);
+        __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, left * kVecBytes);
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const uint32_t vi = u * kBlock + t;
+          v[u] = (vi < left) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) chk.add(v[u]);
+      }
+      if (chk.flagged()) {
+        for (uint32_t vi = t; vi < sp.nvec; vi += kBlock) {
+          __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
+          c += nf_vec<es>(load16(rs, 0), rule);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  __shared__ uint32_t lc[kWaves];
+  if ((t & 63) == 0) lc[t >> 6] = c;
+  __syncthreads();
+  if (t == 0) {
+    for (int i = 1; i < kWaves; ++i) c += lc[i];
+  }
+  return c;
+}
+
+// Signedness does not change the NaN/Inf count; it is dropped here.
+template <class Ty>
+struct Unsigned {
+  typedef TypeTag<Ty::ES, false, Ty::CHK> type;
+};
+
+__global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __restrict__ items,
+                                                           sdc_row* __restrict__ partials,
+                                                           uint64_t* __restrict__ counts,
+                                                           uint64_t* __restrict__ total) {
+  const PlanItem it = items[blockIdx.x];
+  uint32_t c = 0;
+  dispatch_type(it.dtype_flags & ~kItemSigned,
+                [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type>(it); });
+  if (threadIdx.x != 0) return;
+  if (counts) {
+    if (it.dtype_flags & kItemWhole) counts[it.row] = c;
+    else partials[it.slot].nonfinite = c;
+  }
+  // NaN/Inf are rare, so the total's atomics are too.
+  if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
+}
+
+template <class Ty>
+__device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t l) {
+  constexpr uint32_t es = Ty::ES;
+  uint32_t c = 0;
+  if constexpr (Ty::CHK != kChkNone) {
+    const Span sp = span_of<es>(it);
+    const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
+    if (l < sp.h) c += nf_exact(load_elem<es>(sp.base + (uint64_t)l * es), rule);
+    if (l >= 32u && l - 32u < sp.ntail)
+      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - 32u) * es), rule);
+    if (sp.nvec) {
+      __amdgpu_buffer_rsrc_t rs = make_rsrc(sp.base + (uint64_t)sp.h * es, sp.nvec * kVecBytes);
+#pragma unroll
+      for (uint32_t u = 0; u < kWaveVecs; ++u) {
+        const uint32_t vi = u * 64u + l;
+        if (vi < sp.nvec) c += nf_vec<es>(load16(rs, vi * kVecBytes), rule);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  return c;
+}
+
+__global__ void __launch_bounds__(kBlock) nonfinite_small_kernel(const PlanItem* __restrict__ items,
+                                                                 uint32_t n,
+                                                                 uint64_t* __restrict__ counts,
+                                                                 uint64_t* __restrict__ total) {
+  const uint32_t i = wave_item_index();
+  if (i >= n) return;
+  const PlanItem it = items[i];
+  const uint32_t l = threadIdx.x & 63u;
+  uint32_t c = 0;
+  dispatch_type(it.dtype_flags & ~kItemSigned,
+                [&](auto ty) { c = nonfinite_small<typename Unsigned<decltype(ty)>::type>(it, l); });
+  if (l != 0) return;
+  if (counts) counts[it.row] = c;
+  if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
+}
+
+__global__ void __launch_bounds__(kBlock) merge_counts_kernel(const PlanSplit* __restrict__ split,
+                                                              uint32_t n_split,
+                                                              const sdc_row* __restrict__ partials,
+                                                              uint64_t* __restrict__ counts) {
+  const uint32_t e = wave_item_index();
+  if (e >= n_split) return;
+  const PlanSplit sp = split[e];
+  const uint32_t l = threadIdx.x & 63u;
+  uint64_t c = 0;
+  for (uint32_t i = l; i < sp.count; i += 64u) c += partials[sp.first + i].nonfinite;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if (l == 0) counts[sp.row] = c;
+}
+
+__global__ void clear_total_kernel(uint64_t* total) { *total = 0; }
+
+}  // namespace
+}  // namespace sdc
+
+using namespace sdc;
+
+extern "C" int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info,
+                                 uint64_t* d_counts, uint64_t* d_total, sdc_stream_t stream) {
+  if (d_plan == nullptr || h_info == nullptr || d_total == nullptr) return SDC_ERR_INVALID;
+  if (!info_ok(h_info)) return SDC_ERR_PLAN;
+  hipStream_t s = as_stream(stream);
+  const PlanView v = view_of(d_plan, h_info);
+  hipLaunchKernelGGL(clear_total_kernel, dim3(1), dim3(1), 0, s, d_total);
+  int32_t st = launch_status();
+  if (st) return st;
+  const uint64_t n_block = h_info->n_items - h_info->n_small;
+  if (h_info->n_small) {
+    hipLaunchKernelGGL(nonfinite_small_kernel,
+                       dim3((uint32_t)((h_info->n_small + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
+                       v.items + n_block, (uint32_t)h_info->n_small, d_counts, d_total);
+    if ((st = launch_status())) return st;
+  }
+  if (n_block) {
+    hipLaunchKernelGGL(nonfinite_kernel, dim3((uint32_t)n_block), dim3(kBlock), 0, s, v.items,
+                       v.partials, d_counts, d_total);
+    if ((st = launch_status())) return st;
+  }
+  if (d_counts && h_info->n_split) {
+    hipLaunchKernelGGL(merge_counts_kernel,
+                       dim3((uint32_t)((h_info->n_split + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
+                       v.split, (uint32_t)h_info->n_split, v.partials, d_counts);
+    return launch_status();
+  }
+  return SDC_OK;
+}
+

@@ -119,4 +119,28 @@ inline int32_t launch_status() { return hip_status(hipGetLastError()); }
 
 inline hipStream_t as_stream(sdc_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Host-side check that a plan info describes a plan image, and views of the
+// image's parts.
+inline bool info_ok(const sdc_plan_info* h) {
+  if (h == nullptr || h->magic != kPlanMagic || h->n_items > kMaxGrid ||
+      h->n_split > h->n_tensors || h->n_small > h->n_items)
+    return false;
+  return h->plan_bytes >= plan_offsets(h->n_items, h->n_split, h->n_slots).end;
+}
+
+struct PlanView {
+  const PlanItem* items;
+  const PlanSplit* split;
+  sdc_row* partials;
+};
+
+inline PlanView view_of(const void* d_plan, const sdc_plan_info* h) {
+  unsigned char* base = reinterpret_cast<unsigned char*>(const_cast<void*>(d_plan));
+  const PlanOffsets o = plan_offsets(h->n_items, h->n_split, h->n_slots);
+  return PlanView{reinterpret_cast<const PlanItem*>(base + o.items),
+                  reinterpret_cast<const PlanSplit*>(base + o.split),
+                  reinterpret_cast<sdc_row*>(base + o.partials)};
+}
+
+
 }  // namespace sdc
