@@ -15,7 +15,6 @@ namespace {
 template <class Ty>
 __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
   constexpr uint32_t es = Ty::ES;
-  constexpr uint32_t kRound = kBlock * kUnroll;
   const uint32_t t = threadIdx.x;
   uint32_t c = 0;
   if constexpr (Ty::CHK != kChkNone) {  // raw integers are never NaN/Inf: nothing to read
@@ -27,18 +26,7 @@ __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
     if (sp.nvec) {
       const unsigned char* body = sp.base + (uint64_t)sp.h * es;
       Chk<Ty::CHK> chk(rule);
-      for (uint32_t v0 = 0; v0 < sp.nvec; v0 += kRound) {
-        const uint32_t left = min(sp.nvec - v0, kRound);
-        __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, left * kVecBytes);
-        u32x4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const uint32_t vi = u * kBlock + t;
-          v[u] = (vi < left) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) chk.add(v[u]);
-      }
+      stream_body<kCheckU, true>(body, sp.nvec, [&](u32x4 v) { chk.add(v); });
       if (chk.flagged()) {
         for (uint32_t vi = t; vi < sp.nvec; vi += kBlock) {
           __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
@@ -130,7 +118,16 @@ __global__ void __launch_bounds__(kBlock) merge_counts_kernel(const PlanSplit* _
   const PlanSplit sp = split[e];
   const uint32_t l = threadIdx.x & 63u;
   uint64_t c = 0;
-  for (uint32_t i = l; i < sp.count; i += 64u) c += partials[sp.first + i].nonfinite;
+  for (uint32_t i0 = 0; i0 < sp.count; i0 += 64u * kMergeUnroll) {
+    uint64_t v[kMergeUnroll];
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
+      const uint32_t i = i0 + u * 64u + l;
+      v[u] = (i < sp.count) ? partials[sp.first + i].nonfinite : 0u;
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) c += v[u];
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
   if (l == 0) counts[sp.row] = c;

@@ -116,7 +116,6 @@ __device__ __forceinline__ double block_sum_d(double v) {
 template <class Dt>
 __device__ __forceinline__ double sq_item(const PlanItem& it) {
   constexpr uint32_t DT = Dt::DTYPE, es = dt_size<DT>();
-  constexpr uint32_t kRound = kBlock * kUnroll;
   const Span sp = span_of<es>(it);
   const uint32_t t = threadIdx.x;
   double acc = 0.0;
@@ -128,19 +127,10 @@ __device__ __forceinline__ double sq_item(const PlanItem& it) {
     const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + t - 128u) * es));
     acc = __builtin_fma(y, y, acc);
   }
-  const unsigned char* body = sp.base + (uint64_t)sp.h * es;
-  for (uint32_t v0 = 0; v0 < sp.nvec; v0 += kRound) {
-    const uint32_t left = min(sp.nvec - v0, kRound);
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, left * kVecBytes);
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t vi = u * kBlock + t;
-      v[u] = (vi < left) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc = sq_vec<DT>(v[u], acc);
-  }
+  // lane t adds its vectors t, t + 256, t + 512, ... in that order
+  if (sp.nvec)
+    stream_body<kCheckU, true>(sp.base + (uint64_t)sp.h * es, sp.nvec,
+                               [&](u32x4 v) { acc = sq_vec<DT>(v, acc); });
   return acc;
 }
 
@@ -201,8 +191,16 @@ __global__ void __launch_bounds__(kBlock) merge_sq_kernel(const PlanSplit* __res
   const PlanSplit sp = split[e];
   const uint32_t l = threadIdx.x & 63u;
   double acc = 0.0;
-  for (uint32_t i = l; i < sp.count; i += 64u)
-    acc += __longlong_as_double((long long)partials[sp.first + i].sum);
+  for (uint32_t i0 = 0; i0 < sp.count; i0 += 64u * kMergeUnroll) {
+    double v[kMergeUnroll];
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
+      const uint32_t i = i0 + u * 64u + l;
+      v[u] = (i < sp.count) ? __longlong_as_double((long long)partials[sp.first + i].sum) : 0.0;
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) acc += v[u];
+  }
   acc = wave_sum_d(acc);
   if (l == 0) sq[sp.row] = acc;
 }

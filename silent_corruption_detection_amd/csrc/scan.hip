@@ -187,30 +187,6 @@ typedef BodyCfg<8, true> DeepBody;     // ~188 VGPRs: deeper pipeline, 2 workgro
 // Plans whose items average at least this many bytes use DeepBody (measured:
 // better for items of ~170 KiB and more, worse for lists of small tensors).
 constexpr uint64_t kDeepItemBytes = 96ull << 10;
-// Loads round r (vectors r*256*U .. of the body) into v.  Rounds below
-// `full` are complete; the last, partial round masks lanes past the end,
-// whose vectors then read as zero.
-template <int U>
-__device__ __forceinline__ void load_round(const unsigned char* body, uint32_t nvec, uint32_t full,
-                                           uint32_t r, u32x4 (&v)[U]) {
-  constexpr uint32_t kRound = kBlock * U;
-  const uint32_t t = threadIdx.x;
-  const uint32_t v0 = r * kRound;
-  if (r < full) {
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, kRound * kVecBytes);
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = load16(rs, (u * kBlock + t) * kVecBytes);
-  } else {
-    const uint32_t left = nvec - v0;
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, left * kVecBytes);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t vi = u * kBlock + t;
-      v[u] = (vi < left) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
 // Body of one item: nvec aligned vectors at `body`.  Lane t handles vectors
 // 256*it + t, it = 0 .. T-1 with T = rounds*U (uniform over the workgroup);
 // vectors past the end are not loaded and count as zero vectors, which leave
@@ -221,34 +197,9 @@ __device__ __forceinline__ void scan_body(const unsigned char* body, uint32_t nv
   typedef Acc<Ty::ES, Ty::SIGNED, Ty::CHK> A_t;
   constexpr int U = Cfg::U;
   constexpr uint32_t E = kVecBytes / Ty::ES;    // elements per vector
-  constexpr uint32_t kRound = kBlock * U;      // vectors per round
   const uint32_t t = threadIdx.x;
   A_t acc(rule);
-  const uint32_t full = nvec / kRound;
-  const uint32_t rounds = full + ((nvec % kRound) ? 1u : 0u);
-  if constexpr (!Cfg::PIPE) {
-    for (uint32_t r = 0; r < rounds; ++r) {
-      u32x4 v[U];
-      load_round<U>(body, nvec, full, r, v);
-#pragma unroll
-      for (int u = 0; u < U; ++u) acc.add(v[u]);
-    }
-  } else {
-    // Two register sets, alternating, so no copies are needed.
-    u32x4 va[U], vb[U];
-    load_round<U>(body, nvec, full, 0, va);
-    uint32_t r = 0;
-    for (;;) {
-      if (r + 1 < rounds) load_round<U>(body, nvec, full, r + 1, vb);
-#pragma unroll
-      for (int u = 0; u < U; ++u) acc.add(va[u]);
-      if (++r == rounds) break;
-      if (r + 1 < rounds) load_round<U>(body, nvec, full, r + 1, va);
-#pragma unroll
-      for (int u = 0; u < U; ++u) acc.add(vb[u]);
-      if (++r == rounds) break;
-    }
-  }
+  const uint32_t rounds = stream_body<U, Cfg::PIPE>(body, nvec, [&](u32x4 v) { acc.add(v); });
   const uint64_t T = (uint64_t)rounds * U;
   const uint64_t A = acc.sum();
   ln.s += A;
@@ -436,13 +387,24 @@ __global__ void __launch_bounds__(kBlock) merge_rows_kernel(const PlanSplit* __r
   const PlanSplit sp = split[e];
   const uint32_t l = threadIdx.x & 63u;
   Lane ln;
-  for (uint32_t i = l; i < sp.count; i += 64u) {
-    const ulonglong2* p = reinterpret_cast<const ulonglong2*>(partials + sp.first + i);
-    const ulonglong2 a = p[0], b = p[1];
-    ln.s += a.x;
-    ln.w += a.y;
-    ln.x ^= b.x;
-    ln.nf += b.y;
+  const ulonglong2* p = reinterpret_cast<const ulonglong2*>(partials + sp.first);
+  // kMergeUnroll independent slot loads per lane in flight: a tensor split
+  // into thousands of items is merged in a few memory latencies.
+  for (uint32_t i0 = 0; i0 < sp.count; i0 += 64u * kMergeUnroll) {
+    ulonglong2 a[kMergeUnroll], b[kMergeUnroll];
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
+      const uint32_t i = i0 + u * 64u + l;
+      a[u] = (i < sp.count) ? p[2 * i] : ulonglong2{0, 0};
+      b[u] = (i < sp.count) ? p[2 * i + 1] : ulonglong2{0, 0};
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
+      ln.s += a[u].x;
+      ln.w += a[u].y;
+      ln.x ^= b[u].x;
+      ln.nf += b[u].y;
+    }
   }
   wave_reduce(ln);
   if (l != 0) return;

@@ -206,8 +206,74 @@ __device__ __forceinline__ void dispatch_type(uint32_t df, F&& f) {
   }
 }
 
-// Vectors of the nonfinite-only loop per lane per round.
-constexpr int kUnroll = 4;
+// Slot loads per lane in flight in the merge of a split tensor's partial rows.
+constexpr uint32_t kMergeUnroll = 8;
+
+// Vectors per lane per round of the NaN/Inf-count and squared-norm loops
+// (pipelined; these loops hold little state, so a deep pipeline costs no
+// occupancy).
+constexpr int kCheckU = 8;
+
+// Loads round r (vectors r*256*U .. of the body) into v.  Rounds below
+// `full` are complete; the last, partial round masks lanes past the end,
+// whose vectors then read as zero.
+template <int U>
+__device__ __forceinline__ void load_round(const unsigned char* body, uint32_t nvec, uint32_t full,
+                                           uint32_t r, u32x4 (&v)[U]) {
+  constexpr uint32_t kRound = kBlock * U;
+  const uint32_t t = threadIdx.x;
+  const uint32_t v0 = r * kRound;
+  if (r < full) {
+    __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, kRound * kVecBytes);
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load16(rs, (u * kBlock + t) * kVecBytes);
+  } else {
+    const uint32_t left = nvec - v0;
+    __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)v0 * kVecBytes, left * kVecBytes);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t vi = u * kBlock + t;
+      v[u] = (vi < left) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Streams the nvec aligned 16-byte vectors at `body` through consume(v):
+// round r holds vectors r*256*U .. r*256*U + 256*U - 1, lane t taking
+// vectors u*256 + t of each round.  Lanes past the end consume zero vectors.
+// With PIPE the loads of round r+1 are issued before round r is consumed
+// (two register sets, alternating), so a wave keeps loads in flight while it
+// computes.  Requires nvec > 0.  Returns the number of rounds (uniform over
+// the workgroup).
+template <int U, bool PIPE, class F>
+__device__ __forceinline__ uint32_t stream_body(const unsigned char* body, uint32_t nvec, F&& consume) {
+  constexpr uint32_t kRound = kBlock * U;
+  const uint32_t full = nvec / kRound;
+  const uint32_t rounds = full + ((nvec % kRound) ? 1u : 0u);
+  if constexpr (!PIPE) {
+    for (uint32_t r = 0; r < rounds; ++r) {
+      u32x4 v[U];
+      load_round<U>(body, nvec, full, r, v);
+#pragma unroll
+      for (int u = 0; u < U; ++u) consume(v[u]);
+    }
+  } else {
+    u32x4 va[U], vb[U];
+    load_round<U>(body, nvec, full, 0, va);
+    uint32_t r = 0;
+    for (;;) {
+      if (r + 1 < rounds) load_round<U>(body, nvec, full, r + 1, vb);
+#pragma unroll
+      for (int u = 0; u < U; ++u) consume(va[u]);
+      if (++r == rounds) break;
+      if (r + 1 < rounds) load_round<U>(body, nvec, full, r + 1, va);
+#pragma unroll
+      for (int u = 0; u < U; ++u) consume(vb[u]);
+      if (++r == rounds) break;
+    }
+  }
+  return rounds;
+}
 
 // Raw pattern of the ES-byte element at p.
 template <uint32_t ES>
