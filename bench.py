@@ -190,6 +190,44 @@ def bench_other(args, torch, sdc, W_, name):
     return res
 
 
+def bench_recompute(args, torch, sdc, W_):
+    """The recompute audit's scans (a second workload on the scan kernel): per
+    step every checkpointed layer output of a Llama-70B micro-batch is scanned
+    by the plan-free single-tensor path and compared on the device with the row
+    stored at forward time -- one call per tensor, as the hook makes them."""
+    log("bench: generating 80 activation tensors [32768, 8192] bf16 (43 GB) ...")
+    w = W_.recompute_acts("cuda")
+    T = w.T
+    stream = torch.cuda.current_stream()
+    stored = torch.empty((T, 4), dtype=torch.int64, device="cuda")
+    for k in range(T):
+        sdc.sdc_fingerprint_tensor(w.tensors[k], out=stored[k:k + 1], stream=stream)
+    out = torch.empty_like(stored)
+    mis = torch.zeros(T, dtype=torch.int32, device="cuda")
+    # one workspace for all calls: they run in order on the one stream
+    ws = torch.empty(sdc.sdc_tensor_ws_bytes(w.tensors[0]), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        for k in range(T):
+            sdc.sdc_fingerprint_tensor(w.tensors[k], out=out[k:k + 1], ref=stored[k:k + 1],
+                                       mismatch=mis[k:k + 1], stream=stream, ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    ms, kms = time_steps(step, args.steps, args.warmup, stream)
+    if int(mis.sum().item()) != 0 or not torch.equal(out, stored):
+        raise RuntimeError("single-tensor scan is not reproducible")
+    nbytes = sum(t.numel() * t.element_size() for t in w.tensors)
+    return dict(workload=w.name, tensors=T, bytes=nbytes,
+                calls_per_step=T, ms_per_step=round(ms, 4), value=round(nbytes / ms / 1e6, 1),
+                unit="GB/s", kernel_ms=round(kms, 4), kernel_gbs=round(nbytes / kms / 1e6, 1),
+                kernel_frac_of_hbm_peak=round(nbytes / kms / 1e6 / HBM_PEAK_GBS, 4),
+                note="kernel_ms spans the step's 80 scan + compare launch pairs on the stream")
+
+
 def cpu_baseline(w, out, budget_s, sdc, torch):
     """The oracle, single-threaded, on a bounded sample: whole tensors of the
     same list, in list order from layer 0, until the oracle has run budget_s
@@ -228,7 +266,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of single-threaded oracle work in the CPU baseline (0: skip)")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"],
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "recompute"],
                     help="c5 (default) prints the benchmark line; the others print their "
                          "own timing object")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -258,8 +296,12 @@ def main():
         log(f"bench: calibration copy (bitwise_not) of {n} bytes done")
         del src, dst
     if args.workload != "c5":
-        res = (bench_c2(args, torch, sdc, W_) if args.workload == "c2"
-               else bench_other(args, torch, sdc, W_, args.workload))
+        if args.workload == "c2":
+            res = bench_c2(args, torch, sdc, W_)
+        elif args.workload == "recompute":
+            res = bench_recompute(args, torch, sdc, W_)
+        else:
+            res = bench_other(args, torch, sdc, W_, args.workload)
         print(json.dumps(res), flush=True)
         return
     secondary = None

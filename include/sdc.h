@@ -212,6 +212,35 @@ int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, double* d_sq
 int32_t sdc_fingerprint(const sdc_tensor* h_tensors, uint64_t n, void* d_ws, uint64_t ws_bytes,
                         sdc_row* d_out, sdc_stream_t stream);
 
+/* ---- one tensor, no plan ------------------------------------------------- */
+
+/* Device workspace bytes for sdc_fingerprint_tensor on *h_tensor with the
+ * same item_bytes (32 bytes per work item, at least 32).  Host only.  Errors
+ * as sdc_fingerprint_tensor's argument checks. */
+int32_t sdc_tensor_ws_bytes(const sdc_tensor* h_tensor, uint64_t item_bytes, uint64_t* h_bytes);
+
+/* [AEGIS] "core method" item 4: fingerprints of an original result and of its
+ * deterministic recomputation, compared bit for bit; any difference is a
+ * confirmed fault.  Scans ONE tensor without a plan (its work items follow
+ * from its size; the split, and so the row, is that of the list scan) and
+ * writes its row to d_out[0].  With d_ref != NULL (device, one row, e.g. the
+ * row stored when the original was computed) the row is compared with
+ * *d_ref under col_mask (SDC_COL_*), and a difference adds 1 to the device
+ * counter *d_mismatch (required then; the caller clears it).
+ *   h_tensor   host descriptor; ptr is a device pointer (NULL or numel 0: the
+ *              zero row), aligned to the element size; flags: SDC_FLAG_SIGNED.
+ *   item_bytes bytes per work item, a multiple of 16 up to 4 MiB; 0 = automatic
+ *              (about 1024 items, 64 KiB to 1 MiB).  The row does not depend on it.
+ *   d_ws       device workspace of at least sdc_tensor_ws_bytes bytes, not
+ *              reused by the caller before the call's work has completed.
+ * ASYNCHRONOUS on stream, with no host synchronisation and no host-to-device
+ * copy, so it can run inside a backward pass.  Errors: SDC_ERR_INVALID (NULL
+ * d_out / d_ws, d_ref without d_mismatch, bad mask or flags), SDC_ERR_DTYPE,
+ * SDC_ERR_ALIGN, SDC_ERR_RANGE, SDC_ERR_WORKSPACE, SDC_ERR_HIP. */
+int32_t sdc_fingerprint_tensor(const sdc_tensor* h_tensor, uint64_t item_bytes, void* d_ws,
+                               uint64_t ws_bytes, const sdc_row* d_ref, uint32_t col_mask,
+                               sdc_row* d_out, uint32_t* d_mismatch, sdc_stream_t stream);
+
 /* ---- comparisons of fingerprint tables ------------------------------------ */
 
 /* Device workspace bytes for sdc_majority_compare with R replicas, T tensors. */

@@ -21,6 +21,7 @@ __all__ = [
     "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
     "sdc_abi_version", "rows_numpy", "LIB_PATH", "sdc_ring_ws_bytes", "sdc_ring_compare",
     "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS", "sdc_sqnorm",
+    "sdc_tensor_ws_bytes", "sdc_fingerprint_tensor",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
@@ -80,6 +81,8 @@ def _load():
         "sdc_fingerprint_diff": [P, P, U64, U32, P, U64, P, P, U64, P, P],
         "sdc_plan_pack_host": [P, U64, U64, P, U64, P],
         "sdc_sqnorm": [P, P, P, P, P, P],
+        "sdc_tensor_ws_bytes": [P, U64, P],
+        "sdc_fingerprint_tensor": [P, U64, P, U64, P, U32, P, P, P],
         "sdc_ring_ws_bytes": [U32, P],
         "sdc_ring_compare": [P, U32, U64, U32, P, U64, P, P],
         "sdc_ring_localize": [P, U32, U32, P, P],
@@ -259,6 +262,47 @@ def sdc_fingerprint(tensors, out=None, stream=None, signed=False):
     ws.record_stream(s)
     for t in keep:
         t.record_stream(s)
+    return out
+
+
+def sdc_tensor_ws_bytes(t, item_bytes=0, signed=False):
+    arr, _, _ = _descriptors([t], require_contiguous=False, signed=signed)
+    b = ctypes.c_uint64(0)
+    _check(_lib.sdc_tensor_ws_bytes(arr, item_bytes, ctypes.byref(b)), "sdc_tensor_ws_bytes")
+    return b.value
+
+
+def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_ALL, stream=None,
+                           signed=False, item_bytes=0, ws=None):
+    """Row of ONE tensor without a plan (int64 [1, 4] device tensor, or `out`,
+    e.g. a row of a table): asynchronous, no host synchronisation.  With `ref`
+    (a device row), a difference under col_mask adds 1 to `mismatch` (a
+    one-element int32 device tensor the caller cleared).  `ws`: a uint8
+    device workspace of at least sdc_tensor_ws_bytes bytes, reusable by calls
+    on the same stream (they run in order); by default one is allocated."""
+    arr, dev, keep = _descriptors([t], require_contiguous=False, signed=signed)
+    if dev is None:
+        dev = torch.device("cuda")
+    nb = ctypes.c_uint64(0)
+    _check(_lib.sdc_tensor_ws_bytes(arr, item_bytes, ctypes.byref(nb)), "sdc_tensor_ws_bytes")
+    if ws is None or ws.numel() < nb.value:
+        ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    out = _rows_out(out, 1, dev)
+    ref_p = mis_p = None
+    if ref is not None:
+        if ref.dtype != torch.int64 or ref.numel() < 4 or not ref.is_contiguous():
+            raise ValueError("ref must be a contiguous int64 row (4 elements)")
+        if mismatch is None or mismatch.dtype != torch.int32 or mismatch.numel() < 1:
+            raise ValueError("a compare needs a one-element int32 mismatch counter")
+        ref_p, mis_p = ref.data_ptr(), mismatch.data_ptr()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(_lib.sdc_fingerprint_tensor(arr, item_bytes, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                       ctypes.c_void_p(ref_p), col_mask,
+                                       ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(mis_p),
+                                       ctypes.c_void_p(s.cuda_stream)), "sdc_fingerprint_tensor")
+    ws.record_stream(s)
+    for x in keep:
+        x.record_stream(s)
     return out
 
 

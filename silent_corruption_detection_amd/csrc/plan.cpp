@@ -65,10 +65,7 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
     elems += t[k].numel;
     bytes += t[k].numel * es;
   }
-  if (item_bytes == 0) {
-    uint64_t ib = align_up(std::max<uint64_t>(bytes / kAutoTargetItems, 1), 4096);
-    item_bytes = std::min(kAutoMax, std::max(kAutoMin, ib));
-  }
+  if (item_bytes == 0) item_bytes = auto_item_bytes(bytes);
   uint64_t items = 0, small = 0, split = 0, slots = 0;
   for (uint64_t k = 0; k < n; ++k) {
     if (!has_data(t[k])) {

@@ -33,6 +33,8 @@
 //     split tensor stores a partial row in its own slot, and one wave per
 //     split tensor combines its slots (+, +, ^, +: order independent, so the
 //     result is bit-exact, and no atomics share an address).
+#include <algorithm>
+
 #include "scan_device.h"
 
 namespace sdc {
@@ -374,6 +376,33 @@ __global__ void __launch_bounds__(kBlock) fingerprint_small_kernel(const PlanIte
   d[1] = ulonglong2{ln.x, ln.nf};
 }
 
+// One wave combines `count` partial rows at p (+, +, ^, +), lane l taking
+// rows l, l + 64, ...; kMergeUnroll independent row loads per lane are in
+// flight, so a tensor split into thousands of items is merged in a few
+// memory latencies.  The wave's lanes still have to be reduced.
+__device__ __forceinline__ Lane merge_slots(const sdc_row* __restrict__ rows, uint32_t count,
+                                            uint32_t l) {
+  Lane ln;
+  const ulonglong2* p = reinterpret_cast<const ulonglong2*>(rows);
+  for (uint32_t i0 = 0; i0 < count; i0 += 64u * kMergeUnroll) {
+    ulonglong2 a[kMergeUnroll], b[kMergeUnroll];
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
+      const uint32_t i = i0 + u * 64u + l;
+      a[u] = (i < count) ? p[2 * i] : ulonglong2{0, 0};
+      b[u] = (i < count) ? p[2 * i + 1] : ulonglong2{0, 0};
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
+      ln.s += a[u].x;
+      ln.w += a[u].y;
+      ln.x ^= b[u].x;
+      ln.nf += b[u].y;
+    }
+  }
+  return ln;
+}
+
 // Row of each split tensor from its items' partial rows: sums of S and of the
 // already position-offset W (the concatenation identity in additive form),
 // xor of X, sum of NF.  A tensor with no items gets the zero row.  One wave
@@ -386,31 +415,100 @@ __global__ void __launch_bounds__(kBlock) merge_rows_kernel(const PlanSplit* __r
   if (e >= n_split) return;
   const PlanSplit sp = split[e];
   const uint32_t l = threadIdx.x & 63u;
-  Lane ln;
-  const ulonglong2* p = reinterpret_cast<const ulonglong2*>(partials + sp.first);
-  // kMergeUnroll independent slot loads per lane in flight: a tensor split
-  // into thousands of items is merged in a few memory latencies.
-  for (uint32_t i0 = 0; i0 < sp.count; i0 += 64u * kMergeUnroll) {
-    ulonglong2 a[kMergeUnroll], b[kMergeUnroll];
-#pragma unroll
-    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
-      const uint32_t i = i0 + u * 64u + l;
-      a[u] = (i < sp.count) ? p[2 * i] : ulonglong2{0, 0};
-      b[u] = (i < sp.count) ? p[2 * i + 1] : ulonglong2{0, 0};
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < kMergeUnroll; ++u) {
-      ln.s += a[u].x;
-      ln.w += a[u].y;
-      ln.x ^= b[u].x;
-      ln.nf += b[u].y;
-    }
-  }
+  Lane ln = merge_slots(partials + sp.first, sp.count, l);
   wave_reduce(ln);
   if (l != 0) return;
   ulonglong2* d = reinterpret_cast<ulonglong2*>(out + sp.row);
   d[0] = ulonglong2{ln.s, ln.w};
   d[1] = ulonglong2{ln.x, ln.nf};
+}
+
+// ---- one tensor, no plan ---------------------------------------------------------
+// The items of a single tensor follow from the workgroup index alone (the same
+// split a plan makes): item 0 covers the misaligned head and the next ie
+// elements, item i >= 1 the elements [h + i*ie, h + (i+1)*ie).  So the scan
+// needs no plan upload and no host synchronisation.  Every item stores its
+// partial row in slot i of the caller's workspace; one wave merges them.
+struct TensorJob {
+  uint64_t addr, numel, ie;  // base address, elements, elements per item
+  uint32_t h, df;            // misaligned head elements; dtype | kItemSigned
+  uint32_t es, pad;
+};
+
+__device__ __forceinline__ PlanItem job_item(const TensorJob& j, uint32_t i) {
+  const uint64_t start = i ? j.h + (uint64_t)i * j.ie : 0u;
+  const uint64_t end = min(j.numel, (uint64_t)j.h + (uint64_t)(i + 1) * j.ie);
+  PlanItem it;
+  it.addr = j.addr + start * j.es;
+  it.start = start;
+  it.len = (uint32_t)(end - start);
+  it.row = 0;
+  it.slot = i;
+  it.dtype_flags = j.df;
+  return it;
+}
+
+template <class Cfg>
+__global__ void __launch_bounds__(kBlock) fingerprint_tensor_kernel(TensorJob j,
+                                                                    sdc_row* __restrict__ partials) {
+  const PlanItem it = job_item(j, blockIdx.x);
+  Lane ln;
+  dispatch_type(it.dtype_flags, [&](auto ty) { scan_item<decltype(ty), Cfg>(it, ln); });
+  if (threadIdx.x != 0) return;
+  ulonglong2* d = reinterpret_cast<ulonglong2*>(partials + blockIdx.x);
+  d[0] = ulonglong2{ln.s, ln.w + it.start * ln.s};
+  d[1] = ulonglong2{ln.x, ln.nf};
+}
+
+__device__ __forceinline__ bool rows_differ(const sdc_row& a, const sdc_row& b, uint32_t mask) {
+  return ((mask & SDC_COL_SUM) && a.sum != b.sum) || ((mask & SDC_COL_WSUM) && a.wsum != b.wsum) ||
+         ((mask & SDC_COL_XOR) && a.xorsum != b.xorsum) ||
+         ((mask & SDC_COL_NONFINITE) && a.nonfinite != b.nonfinite);
+}
+
+// One wave: the tensor's row from its n partial rows; with a reference row,
+// a difference under the mask adds 1 to *mismatch.
+__global__ void __launch_bounds__(64) merge_check_kernel(const sdc_row* __restrict__ partials,
+                                                         uint32_t n, sdc_row* __restrict__ out,
+                                                         const sdc_row* __restrict__ ref,
+                                                         uint32_t mask, uint32_t* __restrict__ mismatch) {
+  const uint32_t l = threadIdx.x;
+  Lane ln = merge_slots(partials, n, l);
+  wave_reduce(ln);
+  if (l != 0) return;
+  const sdc_row r{ln.s, ln.w, ln.x, ln.nf};
+  ulonglong2* d = reinterpret_cast<ulonglong2*>(out);
+  d[0] = ulonglong2{r.sum, r.wsum};
+  d[1] = ulonglong2{r.xorsum, r.nonfinite};
+  if (ref && rows_differ(r, *ref, mask)) atomicAdd(mismatch, 1u);
+}
+
+// Launch shape of the single-tensor scan: items and the split of item 0.
+struct TensorShape {
+  uint64_t n_items, ie;
+  uint32_t h, es;
+};
+
+int32_t tensor_shape(const sdc_tensor* t, uint64_t item_bytes, TensorShape* sh) {
+  if (t == nullptr) return SDC_ERR_INVALID;
+  if (item_bytes % kVecBytes != 0 || item_bytes > kItemBytesMax) return SDC_ERR_INVALID;
+  if ((t->flags & ~(uint32_t)SDC_FLAG_SIGNED) != 0) return SDC_ERR_INVALID;
+  const uint32_t es = element_size(t->dtype);
+  if (es == 0) return SDC_ERR_DTYPE;
+  if (t->numel >= (1ull << 62)) return SDC_ERR_RANGE;
+  const uint64_t numel = t->ptr ? t->numel : 0u;
+  const uint64_t ptr = reinterpret_cast<uintptr_t>(t->ptr);
+  if (ptr % es != 0) return SDC_ERR_ALIGN;
+  const uint64_t ie = (item_bytes ? item_bytes : tensor_item_bytes(numel * es)) / es;
+  const uint64_t mis = ptr & 15u;
+  const uint64_t h = mis ? std::min<uint64_t>(numel, (16u - mis) / es) : 0u;
+  const uint64_t first = std::min<uint64_t>(numel, h + ie);
+  sh->n_items = numel ? 1 + (numel - first + ie - 1) / ie : 0;
+  if (sh->n_items > kMaxGrid) return SDC_ERR_RANGE;
+  sh->ie = ie;
+  sh->h = (uint32_t)h;
+  sh->es = es;
+  return SDC_OK;
 }
 
 int32_t launch_scan(const void* d_plan, const sdc_plan_info* h, sdc_row* out, hipStream_t s) {
@@ -458,4 +556,49 @@ extern "C" int32_t sdc_fingerprint(const sdc_tensor* h_tensors, uint64_t n, void
   int32_t st = sdc_plan_build(h_tensors, n, 0, d_ws, ws_bytes, &info, stream);
   if (st) return st;
   return sdc_fingerprint_plan(d_ws, &info, d_out, stream);
+}
+
+extern "C" int32_t sdc_tensor_ws_bytes(const sdc_tensor* h_tensor, uint64_t item_bytes,
+                                       uint64_t* h_bytes) {
+  if (h_bytes == nullptr) return SDC_ERR_INVALID;
+  TensorShape sh;
+  const int32_t st = tensor_shape(h_tensor, item_bytes, &sh);
+  if (st) return st;
+  *h_bytes = std::max<uint64_t>(sh.n_items, 1) * sizeof(sdc_row);
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_fingerprint_tensor(const sdc_tensor* h_tensor, uint64_t item_bytes, void* d_ws,
+                                          uint64_t ws_bytes, const sdc_row* d_ref, uint32_t col_mask,
+                                          sdc_row* d_out, uint32_t* d_mismatch, sdc_stream_t stream) {
+  TensorShape sh;
+  int32_t st = tensor_shape(h_tensor, item_bytes, &sh);
+  if (st) return st;
+  if (d_out == nullptr || d_ws == nullptr) return SDC_ERR_INVALID;
+  if (d_ref && (d_mismatch == nullptr || (col_mask & SDC_COL_ALL) == 0 ||
+                (col_mask & ~(uint32_t)SDC_COL_ALL) != 0))
+    return SDC_ERR_INVALID;
+  if (ws_bytes < std::max<uint64_t>(sh.n_items, 1) * sizeof(sdc_row)) return SDC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  sdc_row* partials = reinterpret_cast<sdc_row*>(d_ws);
+  if (sh.n_items) {
+    TensorJob j;
+    j.addr = reinterpret_cast<uintptr_t>(h_tensor->ptr);
+    j.numel = h_tensor->numel;
+    j.ie = sh.ie;
+    j.h = sh.h;
+    j.df = h_tensor->dtype | ((h_tensor->flags & SDC_FLAG_SIGNED) ? kItemSigned : 0u);
+    j.es = sh.es;
+    j.pad = 0;
+    if (sh.ie * sh.es >= kDeepItemBytes)
+      hipLaunchKernelGGL(fingerprint_tensor_kernel<DeepBody>, dim3((uint32_t)sh.n_items), dim3(kBlock),
+                         0, s, j, partials);
+    else
+      hipLaunchKernelGGL(fingerprint_tensor_kernel<DefaultBody>, dim3((uint32_t)sh.n_items),
+                         dim3(kBlock), 0, s, j, partials);
+    if ((st = launch_status())) return st;
+  }
+  hipLaunchKernelGGL(merge_check_kernel, dim3(1), dim3(64), 0, s, partials, (uint32_t)sh.n_items,
+                     d_out, d_ref, col_mask, d_mismatch);
+  return launch_status();
 }

@@ -100,3 +100,68 @@ def test_workspace_sizing():
     assert sdc.sdc_diff_ws_bytes(100, 10) > sdc.sdc_diff_ws_bytes(100, 0)
     with pytest.raises(sdc.SdcError):
         sdc.sdc_majority_ws_bytes(0, 10)
+
+
+def tensor_ws_bytes(desc, item_bytes=0):
+    import silent_corruption_detection_amd as sdc
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    t = _T(*desc)
+    out = ctypes.c_uint64(0)
+    rc = lib.sdc_tensor_ws_bytes(ctypes.byref(t), ctypes.c_uint64(item_bytes), ctypes.byref(out))
+    return rc, out.value
+
+
+def one_tensor_plan_items(desc, item_bytes):
+    import silent_corruption_detection_amd as sdc
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    arr = (_T * 1)(_T(*desc))
+    need = ctypes.c_uint64(0)
+    assert lib.sdc_plan_bytes(arr, ctypes.c_uint64(1), ctypes.c_uint64(item_bytes),
+                              ctypes.byref(need)) == 0
+    buf = (ctypes.c_ubyte * need.value)()
+
+    class Info(ctypes.Structure):
+        _fields_ = [(n, ctypes.c_uint64) for n in ("magic", "n_tensors", "n_items", "n_small",
+                                                    "n_split", "n_slots", "total_elems",
+                                                    "total_bytes", "plan_bytes", "item_bytes")]
+    info = Info()
+    assert lib.sdc_plan_pack_host(arr, ctypes.c_uint64(1), ctypes.c_uint64(item_bytes), buf,
+                                  ctypes.c_uint64(need.value), ctypes.byref(info)) == 0
+    return info.n_items, info.total_bytes
+
+
+DESCS = [(0x10000, 1, 0, 0), (0x10004, 1000, 0, 0), (0x10002, 3 << 20, 1, 0),
+         (0x10000, 5 << 30, 1, 1), (0x10008, 12345678, 3, 0), (0x10003, 7777777, 4, 0)]
+
+
+@pytest.mark.parametrize("desc", DESCS)
+@pytest.mark.parametrize("item_bytes", [16, 4096, 65536, 1 << 20, 4 << 20])
+def test_tensor_ws_bytes_match_the_plan_split(desc, item_bytes):
+    # the single-tensor scan splits a tensor exactly as a one-tensor plan does
+    if desc[1] * 8 // item_bytes > 1 << 22:
+        pytest.skip("plan image too large for a host test")
+    rc, ws = tensor_ws_bytes(desc, item_bytes)
+    assert rc == 0
+    assert ws == 32 * one_tensor_plan_items(desc, item_bytes)[0]
+
+
+@pytest.mark.parametrize("desc", DESCS)
+def test_tensor_automatic_item_size(desc):
+    # about 1024 items, a multiple of 4 KiB within [64 KiB, 1 MiB]
+    nbytes = one_tensor_plan_items(desc, 65536)[1]
+    ib = -(-max(nbytes // 1024, 1) // 4096) * 4096
+    ib = min(max(ib, 64 << 10), 1 << 20)
+    assert tensor_ws_bytes(desc)[1] == 32 * one_tensor_plan_items(desc, ib)[0]
+
+
+@pytest.mark.parametrize("desc,item_bytes,code", [
+    ((0x10000, 10, 99, 0), 0, -2), ((0x10001, 10, 0, 0), 0, -3), ((0x10000, 10, 0, 2), 0, -1),
+    ((0x10000, 1 << 62, 0, 0), 0, -7), ((0x10000, 10, 0, 0), 24, -1),
+    ((0x10000, 10, 0, 0), 8 << 20, -1)])
+def test_tensor_ws_bytes_errors(desc, item_bytes, code):
+    assert tensor_ws_bytes(desc, item_bytes)[0] == code
+
+
+def test_tensor_ws_bytes_empty_and_missing():
+    assert tensor_ws_bytes((None, 100, 0, 0)) == (0, 32)
+    assert tensor_ws_bytes((0x10000, 0, 2, 0)) == (0, 32)

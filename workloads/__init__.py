@@ -302,4 +302,16 @@ def c5_flip(w, seed=55):
     return inj
 
 
+def recompute_acts(device, seed=6, layers=80, tokens=32768, d=8192):
+    """The checkpointed layer outputs of one Llama-70B-shaped micro-batch of
+    8 x 4096 tokens: `layers` hidden-state tensors [tokens, d] in bf16,
+    N(0, 1) (post-norm activations), 512 MiB each -- the input of the
+    recompute audit, one single-tensor scan per layer output."""
+    g = _gen(device, seed)
+    acts = [_normal_(torch.empty((tokens, d), dtype=torch.bfloat16, device=device), 1.0, g)
+            for _ in range(layers)]
+    return Workload(f"recompute_llama70b_acts_{layers}x{tokens}x{d}_bf16", 1, layers, acts,
+                    [f"layer{i}.out" for i in range(layers)], seed)
+
+
 BUILDERS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4, "c5": c5}
