@@ -299,3 +299,32 @@ def test_fp8_and_fp64_special_patterns():
     ref = oracle_rows(tensors)
     assert_rows_equal(rows, ref)
     assert rows[:, 3].tolist() == [2000, 8000, 1000, 1000, 0, 3]
+
+
+@pytest.mark.parametrize("dtype,signed", [(torch.uint8, False), (torch.bfloat16, True),
+                                          (torch.float16, False)])
+def test_tensor_with_more_than_2_32_elements(dtype, signed):
+    # positions i + 1 beyond 2^32 (the weighted sum's 64-bit position products),
+    # through the list scan (automatic and 4 MiB items) and the single-tensor scan
+    es = torch.empty(0, dtype=dtype).element_size()
+    n = (1 << 32) + 12_345
+    raw = torch.empty(n * es + 16, dtype=torch.uint8, device=DEV)
+    g = gen(32)
+    for lo in range(0, raw.numel(), 1 << 30):  # random bytes, 1 GiB at a time
+        hi = min(raw.numel(), lo + (1 << 30))
+        raw[lo:hi].random_(0, 256, generator=g)
+    t = carve(raw, 2 * es if es > 1 else 3, n, dtype)
+    say(f"case >2^32 elements dtype={dtype} signed={signed}: oracle")
+    ref = oracle_rows([t], threads=1, flags=O.SIGNED if signed else 0)
+    for ib in (0, 4 << 20):
+        say(f"case >2^32 elements item_bytes={ib}")
+        plan = sdc.sdc_plan_build([t], item_bytes=ib, signed=signed)
+        out = sdc.sdc_fingerprint_plan(plan)
+        torch.cuda.synchronize()
+        assert_rows_equal(sdc.rows_numpy(out), ref)
+        del plan
+    r = sdc.sdc_fingerprint_tensor(t, signed=signed)
+    torch.cuda.synchronize()
+    assert_rows_equal(sdc.rows_numpy(r), ref)
+    del raw, t
+    torch.cuda.empty_cache()
