@@ -14,6 +14,8 @@
 // sdc_ring_compare / sdc_ring_localize / sdc_confirm_verdict: the ring replay
 //   audit of the same section over an all-gathered [rank][own, replay] table.
 #include <algorithm>
+#include <cstddef>
+#include <cstring>
 #include <vector>
 
 #include "sdc_internal.h"
@@ -39,14 +41,128 @@ __device__ __forceinline__ bool row_eq(const Row4& a, const Row4& b, uint32_t m)
 bool mask_ok(uint32_t m) { return (m & SDC_COL_ALL) != 0 && (m & ~(uint32_t)SDC_COL_ALL) == 0; }
 
 // ---- majority ----------------------------------------------------------------
+// Workspace: [0, 32) counters, [32, 64) the result, [64, 64 + R) one byte per
+// replica (named or not) -- result and flags are contiguous, so one copy
+// brings them to the host -- then, 256-byte aligned, R 32-bit flags.
 struct MajWS {
   unsigned long long n_diff, n_nomaj, first_diff, first_nomaj;
   sdc_majority res;
-  uint32_t pad[4];
 };
-static_assert(sizeof(MajWS) == 80, "majority workspace header");
+static_assert(sizeof(MajWS) == 64, "majority workspace header");
 
-constexpr uint64_t kMajHdr = 128;
+constexpr uint64_t kMajOut = offsetof(MajWS, res);  // result, then the R flag bytes
+constexpr uint64_t kMajSus8 = sizeof(MajWS);
+// Tables this small are compared by one workgroup in one launch (flags and
+// counters in LDS); larger ones by a grid of one lane per tensor.
+constexpr uint32_t kMajFusedMaxR = 1024;
+constexpr uint64_t kMajFusedMaxT = 1024;
+
+uint64_t maj_sus_off(uint32_t R) { return (kMajSus8 + R + 255) / 256 * 256; }
+uint64_t maj_ws_bytes(uint32_t R) { return maj_sus_off(R) + ((uint64_t)R * 4 + 255) / 256 * 256; }
+
+// Where the per-tensor outcome goes: device-wide atomics on the workspace, or
+// LDS atomics of the one-workgroup path.  Both are order independent.
+struct GlobalSink {
+  MajWS* ws;
+  uint32_t* sus;
+  __device__ void diff(uint64_t k) {
+    atomicAdd(&ws->n_diff, 1ull);
+    atomicMin(&ws->first_diff, (unsigned long long)k);
+  }
+  __device__ void nomaj(uint64_t k) {
+    atomicAdd(&ws->n_nomaj, 1ull);
+    atomicMin(&ws->first_nomaj, (unsigned long long)k);
+  }
+  __device__ void suspect(uint32_t r) { atomicOr(&sus[r], 1u); }
+};
+
+struct LdsSink {
+  unsigned long long* c;  // n_diff, n_nomaj, first_diff, first_nomaj
+  uint32_t* sus;
+  __device__ void diff(uint64_t k) {
+    atomicAdd(&c[0], 1ull);
+    atomicMin(&c[2], (unsigned long long)k);
+  }
+  __device__ void nomaj(uint64_t k) {
+    atomicAdd(&c[1], 1ull);
+    atomicMin(&c[3], (unsigned long long)k);
+  }
+  __device__ void suspect(uint32_t r) { atomicOr(&sus[r], 1u); }
+};
+
+// Tensor k: 0 = all R rows equal, 1 = a strict majority (the differing
+// replicas are named), 2 = no strict majority.
+template <class Sink>
+__device__ __forceinline__ uint8_t maj_tensor(const sdc_row* __restrict__ table, uint32_t R,
+                                              uint64_t T, uint64_t k, uint32_t mask, Sink& sink) {
+  const Row4 r0 = load_row(table + k);
+  bool differs = false;
+  for (uint32_t r = 1; r < R && !differs; ++r)
+    differs = !row_eq(load_row(table + (uint64_t)r * T + k), r0, mask);
+  if (!differs) return 0;
+  // Boyer-Moore vote: if some row is held by more than R/2 replicas it is the
+  // surviving candidate; the count below confirms or rejects it.
+  Row4 cand = r0;
+  uint32_t votes = 1;
+  for (uint32_t r = 1; r < R; ++r) {
+    const Row4 v = load_row(table + (uint64_t)r * T + k);
+    if (votes == 0) {
+      cand = v;
+      votes = 1;
+    } else if (row_eq(v, cand, mask)) {
+      votes++;
+    } else {
+      votes--;
+    }
+  }
+  uint32_t c = 0;
+  for (uint32_t r = 0; r < R; ++r) c += row_eq(load_row(table + (uint64_t)r * T + k), cand, mask);
+  sink.diff(k);
+  if (2ull * c > (uint64_t)R) {
+    for (uint32_t r = 0; r < R; ++r)
+      if (!row_eq(load_row(table + (uint64_t)r * T + k), cand, mask)) sink.suspect(r);
+    return 1;
+  }
+  sink.nomaj(k);
+  return 2;
+}
+
+// The result from the counters: with no strict majority somewhere no replica
+// is named.  Executed by one workgroup.
+__device__ __forceinline__ void maj_result(const unsigned long long* c, const uint32_t* sus,
+                                           uint32_t R, MajWS* ws, uint8_t* sus8) {
+  const bool none = c[1] != 0;
+  for (uint32_t r = threadIdx.x; r < R; r += kBlock) sus8[r] = (!none && sus[r]) ? 1 : 0;
+  if (threadIdx.x == 0) {
+    ws->res.diverged = c[0] != 0;
+    ws->res.has_majority = c[1] == 0;
+    ws->res.n_diff = c[0];
+    ws->res.first_diff = c[2];
+    ws->res.first_no_majority = c[3];
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) maj_fused(const sdc_row* __restrict__ table, uint32_t R,
+                                                    uint64_t T, uint32_t mask, MajWS* ws,
+                                                    uint8_t* sus8, uint8_t* status) {
+  __shared__ unsigned long long c[4];
+  __shared__ uint32_t sus[kMajFusedMaxR];
+  if (threadIdx.x == 0) {
+    c[0] = 0;
+    c[1] = 0;
+    c[2] = ~0ull;
+    c[3] = ~0ull;
+  }
+  for (uint32_t r = threadIdx.x; r < R; r += kBlock) sus[r] = 0;
+  __syncthreads();
+  LdsSink sink{c, sus};
+  for (uint64_t k = threadIdx.x; k < T; k += kBlock) {
+    const uint8_t st = maj_tensor(table, R, T, k, mask, sink);
+    if (status) status[k] = st;
+  }
+  __syncthreads();
+  maj_result(c, sus, R, ws, sus8);
+}
 
 __global__ void __launch_bounds__(kBlock) maj_init(MajWS* ws, uint32_t* sus, uint32_t R) {
   const uint32_t i0 = blockIdx.x * kBlock + threadIdx.x;
@@ -62,62 +178,18 @@ __global__ void __launch_bounds__(kBlock) maj_init(MajWS* ws, uint32_t* sus, uin
 __global__ void __launch_bounds__(kBlock) maj_compare(const sdc_row* __restrict__ table, uint32_t R,
                                                       uint64_t T, uint32_t mask, MajWS* ws,
                                                       uint32_t* sus, uint8_t* status) {
+  GlobalSink sink{ws, sus};
   for (uint64_t k = (uint64_t)blockIdx.x * kBlock + threadIdx.x; k < T;
        k += (uint64_t)gridDim.x * kBlock) {
-    const Row4 r0 = load_row(table + k);
-    bool differs = false;
-    for (uint32_t r = 1; r < R && !differs; ++r)
-      differs = !row_eq(load_row(table + (uint64_t)r * T + k), r0, mask);
-    uint8_t st = 0;
-    if (differs) {
-      // Boyer-Moore vote: if some row is held by more than R/2 replicas it is
-      // the surviving candidate; the count below confirms or rejects it.
-      Row4 cand = r0;
-      uint32_t votes = 1;
-      for (uint32_t r = 1; r < R; ++r) {
-        const Row4 v = load_row(table + (uint64_t)r * T + k);
-        if (votes == 0) {
-          cand = v;
-          votes = 1;
-        } else if (row_eq(v, cand, mask)) {
-          votes++;
-        } else {
-          votes--;
-        }
-      }
-      uint32_t c = 0;
-      for (uint32_t r = 0; r < R; ++r) c += row_eq(load_row(table + (uint64_t)r * T + k), cand, mask);
-      atomicAdd(&ws->n_diff, 1ull);
-      atomicMin(&ws->first_diff, (unsigned long long)k);
-      if (2ull * c > (uint64_t)R) {
-        st = 1;
-        for (uint32_t r = 0; r < R; ++r)
-          if (!row_eq(load_row(table + (uint64_t)r * T + k), cand, mask)) atomicOr(&sus[r], 1u);
-      } else {
-        st = 2;
-        atomicAdd(&ws->n_nomaj, 1ull);
-        atomicMin(&ws->first_nomaj, (unsigned long long)k);
-      }
-    }
+    const uint8_t st = maj_tensor(table, R, T, k, mask, sink);
     if (status) status[k] = st;
   }
 }
 
 __global__ void __launch_bounds__(kBlock) maj_finalize(MajWS* ws, const uint32_t* sus, uint8_t* sus8,
                                                        uint32_t R) {
-  const bool none = ws->n_nomaj != 0;  // no strict majority somewhere: name no one
-  for (uint32_t r = threadIdx.x; r < R; r += kBlock) sus8[r] = (!none && sus[r]) ? 1 : 0;
-  if (threadIdx.x == 0) {
-    ws->res.diverged = ws->n_diff != 0;
-    ws->res.has_majority = ws->n_nomaj == 0;
-    ws->res.n_diff = ws->n_diff;
-    ws->res.first_diff = ws->first_diff;
-    ws->res.first_no_majority = ws->first_nomaj;
-  }
-}
-
-uint64_t maj_ws_bytes(uint32_t R) {
-  return kMajHdr + ((uint64_t)R * 4 + 255) / 256 * 256 + ((uint64_t)R + 255) / 256 * 256;
+  const unsigned long long c[4] = {ws->n_diff, ws->n_nomaj, ws->first_diff, ws->first_nomaj};
+  maj_result(c, sus, R, ws, sus8);
 }
 
 // ---- diff --------------------------------------------------------------------
@@ -216,40 +288,71 @@ __global__ void __launch_bounds__(kBlock) diff_scan(const unsigned long long* co
   if (threadIdx.x == 0) *n_diff = carry;
 }
 
-__global__ void __launch_bounds__(kBlock) diff_write(const sdc_row* __restrict__ a,
-                                                     const sdc_row* __restrict__ b, uint64_t T,
-                                                     uint32_t mask,
-                                                     const unsigned long long* offsets,
-                                                     uint64_t* idx, sdc_flip_hint* hints,
-                                                     uint64_t cap) {
-  const uint64_t k0 = (uint64_t)blockIdx.x * kPerBlock + (uint64_t)threadIdx.x * kPerLane;
-  const uint32_t f = lane_flags(a, b, T, mask, k0);
-  uint32_t tot;
-  uint64_t pos = offsets[blockIdx.x] + block_exscan(__popc(f), &tot);
+// One differing row: its index and, when asked for, its flip localisation.
+// Records are contiguous after the count, so one copy usually brings the
+// whole answer to the host.
+struct DiffRec {
+  uint64_t index;
+  sdc_flip_hint hint;
+};
+static_assert(sizeof(DiffRec) == 24, "diff record layout");
+
+__device__ __forceinline__ void write_recs(const sdc_row* __restrict__ a,
+                                           const sdc_row* __restrict__ b, uint64_t k0, uint32_t f,
+                                           uint64_t pos, DiffRec* recs, bool hints, uint64_t cap) {
 #pragma unroll
   for (uint32_t j = 0; j < kPerLane; ++j) {
     if (!(f & (1u << j))) continue;
     if (pos < cap) {
       const uint64_t k = k0 + j;
-      idx[pos] = k;
-      if (hints) hints[pos] = flip_hint(load_row(a + k), load_row(b + k));
+      recs[pos].index = k;
+      if (hints) recs[pos].hint = flip_hint(load_row(a + k), load_row(b + k));
     }
     pos++;
   }
 }
 
+__global__ void __launch_bounds__(kBlock) diff_write(const sdc_row* __restrict__ a,
+                                                     const sdc_row* __restrict__ b, uint64_t T,
+                                                     uint32_t mask,
+                                                     const unsigned long long* offsets,
+                                                     DiffRec* recs, bool hints, uint64_t cap) {
+  const uint64_t k0 = (uint64_t)blockIdx.x * kPerBlock + (uint64_t)threadIdx.x * kPerLane;
+  const uint32_t f = lane_flags(a, b, T, mask, k0);
+  uint32_t tot;
+  const uint64_t pos = offsets[blockIdx.x] + block_exscan(__popc(f), &tot);
+  write_recs(a, b, k0, f, pos, recs, hints, cap);
+}
+
+// Tables of at most one block's rows: count, offsets and records in one launch.
+__global__ void __launch_bounds__(kBlock) diff_fused(const sdc_row* __restrict__ a,
+                                                     const sdc_row* __restrict__ b, uint64_t T,
+                                                     uint32_t mask, unsigned long long* n_diff,
+                                                     DiffRec* recs, bool hints, uint64_t cap) {
+  const uint64_t k0 = (uint64_t)threadIdx.x * kPerLane;
+  const uint32_t f = lane_flags(a, b, T, mask, k0);
+  uint32_t tot;
+  const uint64_t pos = block_exscan(__popc(f), &tot);
+  write_recs(a, b, k0, f, pos, recs, hints, cap);
+  if (threadIdx.x == 0) *n_diff = tot;
+}
+
+// Workspace: [0, 8) the count, [16, 16 + 24 cap) the records, then the
+// per-block counts and offsets of the multi-block pass.
 struct DiffLayout {
-  uint64_t nb, counts_off, offsets_off, idx_off, hints_off, bytes;
+  uint64_t nb, recs_off, counts_off, offsets_off, bytes;
 };
+
+// Records copied together with the count (a second copy only for more).
+constexpr uint64_t kDiffInline = 16;
 
 DiffLayout diff_layout(uint64_t T, uint64_t cap) {
   DiffLayout L;
   L.nb = (T + kPerBlock - 1) / kPerBlock;
-  L.counts_off = 256;
+  L.recs_off = 16;
+  L.counts_off = (L.recs_off + cap * sizeof(DiffRec) + 255) / 256 * 256;
   L.offsets_off = L.counts_off + (L.nb * 8 + 255) / 256 * 256;
-  L.idx_off = L.offsets_off + (L.nb * 8 + 255) / 256 * 256;
-  L.hints_off = L.idx_off + (cap * 8 + 255) / 256 * 256;
-  L.bytes = L.hints_off + (cap * sizeof(sdc_flip_hint) + 255) / 256 * 256;
+  L.bytes = L.offsets_off + (L.nb * 8 + 255) / 256 * 256;
   return L;
 }
 
@@ -388,22 +491,34 @@ extern "C" int32_t sdc_majority_compare(const sdc_row* d_table, uint32_t R, uint
   hipStream_t s = as_stream(stream);
   unsigned char* base = reinterpret_cast<unsigned char*>(d_ws);
   MajWS* ws = reinterpret_cast<MajWS*>(base);
-  uint32_t* sus = reinterpret_cast<uint32_t*>(base + kMajHdr);
-  uint8_t* sus8 = base + kMajHdr + ((uint64_t)R * 4 + 255) / 256 * 256;
-  const uint32_t gi = (uint32_t)std::min<uint64_t>((R + kBlock - 1) / kBlock, 1024);
-  hipLaunchKernelGGL(maj_init, dim3(gi), dim3(kBlock), 0, s, ws, sus, R);
-  int32_t st = launch_status();
-  if (st) return st;
-  const uint32_t gc = (uint32_t)std::min<uint64_t>((T + kBlock - 1) / kBlock, 4096);
-  hipLaunchKernelGGL(maj_compare, dim3(gc), dim3(kBlock), 0, s, d_table, R, T, col_mask, ws, sus,
-                     d_tensor_status);
-  if ((st = launch_status())) return st;
-  hipLaunchKernelGGL(maj_finalize, dim3(1), dim3(kBlock), 0, s, ws, sus, sus8, R);
-  if ((st = launch_status())) return st;
-  if ((st = hip_status(hipMemcpyAsync(h_res, &ws->res, sizeof(sdc_majority), hipMemcpyDeviceToHost, s))))
+  uint8_t* sus8 = base + kMajSus8;
+  uint32_t* sus = reinterpret_cast<uint32_t*>(base + maj_sus_off(R));
+  int32_t st;
+  if (R <= kMajFusedMaxR && T <= kMajFusedMaxT) {
+    hipLaunchKernelGGL(maj_fused, dim3(1), dim3(kBlock), 0, s, d_table, R, T, col_mask, ws, sus8,
+                       d_tensor_status);
+    if ((st = launch_status())) return st;
+  } else {
+    const uint32_t gi = (uint32_t)std::min<uint64_t>((R + kBlock - 1) / kBlock, 1024);
+    hipLaunchKernelGGL(maj_init, dim3(gi), dim3(kBlock), 0, s, ws, sus, R);
+    if ((st = launch_status())) return st;
+    const uint32_t gc = (uint32_t)std::min<uint64_t>((T + kBlock - 1) / kBlock, 4096);
+    hipLaunchKernelGGL(maj_compare, dim3(gc), dim3(kBlock), 0, s, d_table, R, T, col_mask, ws, sus,
+                       d_tensor_status);
+    if ((st = launch_status())) return st;
+    hipLaunchKernelGGL(maj_finalize, dim3(1), dim3(kBlock), 0, s, ws, sus, sus8, R);
+    if ((st = launch_status())) return st;
+  }
+  // one copy of the result and the flag bytes, then split on the host
+  thread_local std::vector<unsigned char> stage;
+  stage.resize(sizeof(sdc_majority) + R);
+  if ((st = hip_status(hipMemcpyAsync(stage.data(), base + kMajOut, stage.size(),
+                                      hipMemcpyDeviceToHost, s))))
     return st;
-  if ((st = hip_status(hipMemcpyAsync(h_suspect, sus8, R, hipMemcpyDeviceToHost, s)))) return st;
-  return hip_status(hipStreamSynchronize(s));
+  if ((st = hip_status(hipStreamSynchronize(s)))) return st;
+  std::memcpy(h_res, stage.data(), sizeof(sdc_majority));
+  std::memcpy(h_suspect, stage.data() + sizeof(sdc_majority), R);
+  return SDC_OK;
 }
 
 extern "C" int32_t sdc_diff_ws_bytes(uint64_t T, uint64_t idx_cap, uint64_t* h_bytes) {
@@ -431,31 +546,48 @@ extern "C" int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, 
   hipStream_t s = as_stream(stream);
   unsigned char* base = reinterpret_cast<unsigned char*>(d_ws);
   unsigned long long* n_diff = reinterpret_cast<unsigned long long*>(base);
-  unsigned long long* counts = reinterpret_cast<unsigned long long*>(base + L.counts_off);
-  unsigned long long* offsets = reinterpret_cast<unsigned long long*>(base + L.offsets_off);
-  uint64_t* idx = reinterpret_cast<uint64_t*>(base + L.idx_off);
-  sdc_flip_hint* hints = reinterpret_cast<sdc_flip_hint*>(base + L.hints_off);
+  DiffRec* recs = reinterpret_cast<DiffRec*>(base + L.recs_off);
+  const bool hints = h_hints != nullptr;
   int32_t st;
-  hipLaunchKernelGGL(diff_count, dim3((uint32_t)L.nb), dim3(kBlock), 0, s, d_a, d_b, T, col_mask,
-                     counts);
-  if ((st = launch_status())) return st;
-  hipLaunchKernelGGL(diff_scan, dim3(1), dim3(kBlock), 0, s, counts, offsets, L.nb, n_diff);
-  if ((st = launch_status())) return st;
-  hipLaunchKernelGGL(diff_write, dim3((uint32_t)L.nb), dim3(kBlock), 0, s, d_a, d_b, T, col_mask,
-                     offsets, idx, h_hints ? hints : nullptr, idx_cap);
-  if ((st = launch_status())) return st;
-  uint64_t n = 0;
-  if ((st = hip_status(hipMemcpyAsync(&n, n_diff, 8, hipMemcpyDeviceToHost, s)))) return st;
+  if (L.nb == 1) {
+    hipLaunchKernelGGL(diff_fused, dim3(1), dim3(kBlock), 0, s, d_a, d_b, T, col_mask, n_diff, recs,
+                       hints, idx_cap);
+    if ((st = launch_status())) return st;
+  } else {
+    unsigned long long* counts = reinterpret_cast<unsigned long long*>(base + L.counts_off);
+    unsigned long long* offsets = reinterpret_cast<unsigned long long*>(base + L.offsets_off);
+    hipLaunchKernelGGL(diff_count, dim3((uint32_t)L.nb), dim3(kBlock), 0, s, d_a, d_b, T, col_mask,
+                       counts);
+    if ((st = launch_status())) return st;
+    hipLaunchKernelGGL(diff_scan, dim3(1), dim3(kBlock), 0, s, counts, offsets, L.nb, n_diff);
+    if ((st = launch_status())) return st;
+    hipLaunchKernelGGL(diff_write, dim3((uint32_t)L.nb), dim3(kBlock), 0, s, d_a, d_b, T, col_mask,
+                       offsets, recs, hints, idx_cap);
+    if ((st = launch_status())) return st;
+  }
+  // The count and the first records in one copy; the rest only if there are more.
+  const uint64_t first = std::min(idx_cap, kDiffInline);
+  thread_local std::vector<unsigned char> stage;
+  stage.resize(L.recs_off + idx_cap * sizeof(DiffRec));
+  if ((st = hip_status(hipMemcpyAsync(stage.data(), base, L.recs_off + first * sizeof(DiffRec),
+                                      hipMemcpyDeviceToHost, s))))
+    return st;
   if ((st = hip_status(hipStreamSynchronize(s)))) return st;
+  uint64_t n;
+  std::memcpy(&n, stage.data(), 8);
   *h_n_diff = n;
   const uint64_t m = std::min(n, idx_cap);
-  if (m) {
-    if ((st = hip_status(hipMemcpyAsync(h_idx, idx, m * 8, hipMemcpyDeviceToHost, s)))) return st;
-    if (h_hints &&
-        (st = hip_status(hipMemcpyAsync(h_hints, hints, m * sizeof(sdc_flip_hint),
-                                        hipMemcpyDeviceToHost, s))))
+  if (m > first) {
+    if ((st = hip_status(hipMemcpyAsync(stage.data() + L.recs_off + first * sizeof(DiffRec),
+                                        base + L.recs_off + first * sizeof(DiffRec),
+                                        (m - first) * sizeof(DiffRec), hipMemcpyDeviceToHost, s))))
       return st;
     if ((st = hip_status(hipStreamSynchronize(s)))) return st;
+  }
+  const DiffRec* r = reinterpret_cast<const DiffRec*>(stage.data() + L.recs_off);
+  for (uint64_t i = 0; i < m; ++i) {
+    h_idx[i] = r[i].index;
+    if (hints) h_hints[i] = r[i].hint;
   }
   return SDC_OK;
 }

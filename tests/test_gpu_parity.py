@@ -201,6 +201,22 @@ def test_majority_matches_oracle(R):
                 assert np.array_equal(status.cpu().numpy(), ref["tensor_status"])
 
 
+@pytest.mark.parametrize("R,T", [(1024, 3), (1025, 3), (3, 1024), (3, 1025), (1100, 40)])
+def test_majority_one_workgroup_and_grid_paths(R, T):
+    # tables of at most 1024 replicas and 1024 tensors take the one-workgroup
+    # path; the boundary cases on either side must agree with the oracle
+    rng = np.random.default_rng(R * 7 + T)
+    for p in (0.0, 0.002, 0.05):
+        table = random_table(R, T, rng, p, palette=2)
+        say(f"case majority paths R={R} T={T} p={p}")
+        got = sdc.sdc_majority_compare(to_dev(table), R, T)
+        ref = O.majority_compare(table, R, T, O.COL_ALL)
+        for key in ("diverged", "has_majority", "n_diff", "first_diff", "first_no_majority",
+                    "suspects"):
+            assert got[key] == ref[key], (key, got[key], ref[key])
+        assert np.array_equal(got["suspect_flags"], ref["suspect_flags"])
+
+
 def test_majority_rejects_bad_arguments():
     t = to_dev(np.zeros((3, 4), dtype=np.uint64))
     with pytest.raises(sdc.SdcError):
@@ -234,6 +250,8 @@ def test_diff_matches_oracle():
                 assert got["n_diff"] == ref["n_diff"]
                 assert got["indices"] == ref["indices"]
                 assert got["hints"] == ref["hints"]
+        got = sdc.sdc_fingerprint_diff(to_dev(a), to_dev(b), hints=False)
+        assert got["indices"] == O.fingerprint_diff(a, b, O.COL_ALL, cap=T)["indices"]
 
 
 # ---------------------------------------------------------------------------
