@@ -29,6 +29,7 @@ METRIC = "fingerprint scan GB/s (and % of HBM peak) on ~1B fp32 and 70B bf16 par
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 # Everything the profiled fingerprint kernel and its launch plan are built from.
 KERNEL_SOURCES = ["silent_corruption_detection_amd/csrc/scan.hip",
+                  "silent_corruption_detection_amd/csrc/fingerprint_device.h",
                   "silent_corruption_detection_amd/csrc/scan_device.h",
                   "silent_corruption_detection_amd/csrc/plan.cpp",
                   "silent_corruption_detection_amd/csrc/sdc_internal.h"]

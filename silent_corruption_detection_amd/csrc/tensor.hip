@@ -1,0 +1,149 @@
+// tensor.hip -- the fingerprint of ONE tensor without a plan, with an
+// on-device compare against a stored row: the recompute check of the AEGIS
+// review page ("Safeguarding LLM Training at Scale"), section "core method",
+// item 4 (fingerprints of an original and of its deterministic
+// recomputation, compared bit for bit), for gfx950.
+#include <algorithm>
+
+#include "fingerprint_device.h"
+
+namespace sdc {
+namespace {
+
+// ---- one tensor, no plan ---------------------------------------------------------
+// The items of a single tensor follow from the workgroup index alone (the same
+// split a plan makes): item 0 covers the misaligned head and the next ie
+// elements, item i >= 1 the elements [h + i*ie, h + (i+1)*ie).  So the scan
+// needs no plan upload and no host synchronisation.  Every item stores its
+// partial row in slot i of the caller's workspace; one wave merges them.
+struct TensorJob {
+  uint64_t addr, numel, ie;  // base address, elements, elements per item
+  uint32_t h, df;            // misaligned head elements; dtype | kItemSigned
+  uint32_t es, pad;
+};
+
+__device__ __forceinline__ PlanItem job_item(const TensorJob& j, uint32_t i) {
+  const uint64_t start = i ? j.h + (uint64_t)i * j.ie : 0u;
+  const uint64_t end = min(j.numel, (uint64_t)j.h + (uint64_t)(i + 1) * j.ie);
+  PlanItem it;
+  it.addr = j.addr + start * j.es;
+  it.start = start;
+  it.len = (uint32_t)(end - start);
+  it.row = 0;
+  it.slot = i;
+  it.dtype_flags = j.df;
+  return it;
+}
+
+template <class Cfg>
+__global__ void __launch_bounds__(kBlock) fingerprint_tensor_kernel(TensorJob j,
+                                                                    sdc_row* __restrict__ partials) {
+  const PlanItem it = job_item(j, blockIdx.x);
+  Lane ln;
+  dispatch_type(it.dtype_flags, [&](auto ty) { scan_item<decltype(ty), Cfg>(it, ln); });
+  if (threadIdx.x != 0) return;
+  ulonglong2* d = reinterpret_cast<ulonglong2*>(partials + blockIdx.x);
+  d[0] = ulonglong2{ln.s, ln.w + it.start * ln.s};
+  d[1] = ulonglong2{ln.x, ln.nf};
+}
+
+__device__ __forceinline__ bool rows_differ(const sdc_row& a, const sdc_row& b, uint32_t mask) {
+  return ((mask & SDC_COL_SUM) && a.sum != b.sum) || ((mask & SDC_COL_WSUM) && a.wsum != b.wsum) ||
+         ((mask & SDC_COL_XOR) && a.xorsum != b.xorsum) ||
+         ((mask & SDC_COL_NONFINITE) && a.nonfinite != b.nonfinite);
+}
+
+// One workgroup: the tensor's row from its n partial rows; with a reference
+// row, a difference under the mask adds 1 to *mismatch.
+__global__ void __launch_bounds__(kBlock) merge_check_kernel(const sdc_row* __restrict__ partials,
+                                                             uint32_t n, sdc_row* __restrict__ out,
+                                                             const sdc_row* __restrict__ ref,
+                                                             uint32_t mask,
+                                                             uint32_t* __restrict__ mismatch) {
+  Lane ln = merge_slots<kBlock>(partials, n, threadIdx.x);
+  block_reduce(ln);
+  if (threadIdx.x != 0) return;
+  const sdc_row r{ln.s, ln.w, ln.x, ln.nf};
+  ulonglong2* d = reinterpret_cast<ulonglong2*>(out);
+  d[0] = ulonglong2{r.sum, r.wsum};
+  d[1] = ulonglong2{r.xorsum, r.nonfinite};
+  if (ref && rows_differ(r, *ref, mask)) atomicAdd(mismatch, 1u);
+}
+
+// Launch shape of the single-tensor scan: items and the split of item 0.
+struct TensorShape {
+  uint64_t n_items, ie;
+  uint32_t h, es;
+};
+
+int32_t tensor_shape(const sdc_tensor* t, uint64_t item_bytes, TensorShape* sh) {
+  if (t == nullptr) return SDC_ERR_INVALID;
+  if (item_bytes % kVecBytes != 0 || item_bytes > kItemBytesMax) return SDC_ERR_INVALID;
+  if ((t->flags & ~(uint32_t)SDC_FLAG_SIGNED) != 0) return SDC_ERR_INVALID;
+  const uint32_t es = element_size(t->dtype);
+  if (es == 0) return SDC_ERR_DTYPE;
+  if (t->numel >= (1ull << 62)) return SDC_ERR_RANGE;
+  const uint64_t numel = t->ptr ? t->numel : 0u;
+  const uint64_t ptr = reinterpret_cast<uintptr_t>(t->ptr);
+  if (ptr % es != 0) return SDC_ERR_ALIGN;
+  const uint64_t ie = (item_bytes ? item_bytes : tensor_item_bytes(numel * es)) / es;
+  const uint64_t mis = ptr & 15u;
+  const uint64_t h = mis ? std::min<uint64_t>(numel, (16u - mis) / es) : 0u;
+  const uint64_t first = std::min<uint64_t>(numel, h + ie);
+  sh->n_items = numel ? 1 + (numel - first + ie - 1) / ie : 0;
+  if (sh->n_items > kMaxGrid) return SDC_ERR_RANGE;
+  sh->ie = ie;
+  sh->h = (uint32_t)h;
+  sh->es = es;
+  return SDC_OK;
+}
+
+}  // namespace
+}  // namespace sdc
+
+using namespace sdc;
+
+extern "C" int32_t sdc_tensor_ws_bytes(const sdc_tensor* h_tensor, uint64_t item_bytes,
+                                       uint64_t* h_bytes) {
+  if (h_bytes == nullptr) return SDC_ERR_INVALID;
+  TensorShape sh;
+  const int32_t st = tensor_shape(h_tensor, item_bytes, &sh);
+  if (st) return st;
+  *h_bytes = std::max<uint64_t>(sh.n_items, 1) * sizeof(sdc_row);
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_fingerprint_tensor(const sdc_tensor* h_tensor, uint64_t item_bytes, void* d_ws,
+                                          uint64_t ws_bytes, const sdc_row* d_ref, uint32_t col_mask,
+                                          sdc_row* d_out, uint32_t* d_mismatch, sdc_stream_t stream) {
+  TensorShape sh;
+  int32_t st = tensor_shape(h_tensor, item_bytes, &sh);
+  if (st) return st;
+  if (d_out == nullptr || d_ws == nullptr) return SDC_ERR_INVALID;
+  if (d_ref && (d_mismatch == nullptr || (col_mask & SDC_COL_ALL) == 0 ||
+                (col_mask & ~(uint32_t)SDC_COL_ALL) != 0))
+    return SDC_ERR_INVALID;
+  if (ws_bytes < std::max<uint64_t>(sh.n_items, 1) * sizeof(sdc_row)) return SDC_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  sdc_row* partials = reinterpret_cast<sdc_row*>(d_ws);
+  if (sh.n_items) {
+    TensorJob j;
+    j.addr = reinterpret_cast<uintptr_t>(h_tensor->ptr);
+    j.numel = h_tensor->numel;
+    j.ie = sh.ie;
+    j.h = sh.h;
+    j.df = h_tensor->dtype | ((h_tensor->flags & SDC_FLAG_SIGNED) ? kItemSigned : 0u);
+    j.es = sh.es;
+    j.pad = 0;
+    if (sh.ie * sh.es >= kDeepItemBytes)
+      hipLaunchKernelGGL(fingerprint_tensor_kernel<DeepBody>, dim3((uint32_t)sh.n_items), dim3(kBlock),
+                         0, s, j, partials);
+    else
+      hipLaunchKernelGGL(fingerprint_tensor_kernel<DefaultBody>, dim3((uint32_t)sh.n_items),
+                         dim3(kBlock), 0, s, j, partials);
+    if ((st = launch_status())) return st;
+  }
+  hipLaunchKernelGGL(merge_check_kernel, dim3(1), dim3(kBlock), 0, s, partials,
+                     (uint32_t)sh.n_items, d_out, d_ref, col_mask, d_mismatch);
+  return launch_status();
+}
