@@ -300,9 +300,12 @@ def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_AL
                                        ctypes.c_void_p(ref_p), col_mask,
                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(mis_p),
                                        ctypes.c_void_p(s.cuda_stream)), "sdc_fingerprint_tensor")
-    ws.record_stream(s)
-    for x in keep:
-        x.record_stream(s)
+    if not torch.cuda.is_current_stream_capturing():
+        # keep the workspace and any contiguous copy alive until the scan ran
+        # (under graph capture they belong to the graph's memory pool instead)
+        ws.record_stream(s)
+        for x in keep:
+            x.record_stream(s)
     return out
 
 
