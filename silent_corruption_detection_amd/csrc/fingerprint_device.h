@@ -268,11 +268,24 @@ __device__ __forceinline__ void scan_item(const PlanItem& it, Lane& ln) {
   ln.x = finish_xor<Ty>(ln.x);
 }
 
-// ---- wave items: small tensors, one wave each ---------------------------------
-// The aligned body has at most 64 x kWaveVecs vectors; lane l loads vectors
-// 64*u + l for u = 0 .. kWaveVecs-1 all at once (T = kWaveVecs, missing
-// vectors count as zero), then W_lane = (h+1+E*l)*A + 64*E*(T*A - Q) + C.
-template <class Ty>
+// ---- wave items: small tensors, one wave or half a wave each --------------------
+// The aligned body has at most LANES x kWaveVecs vectors; lane l loads vectors
+// LANES*u + l for u = 0 .. kWaveVecs-1 all at once (T = kWaveVecs, missing
+// vectors count as zero), then W_lane = (h+1+E*l)*A + LANES*E*(T*A - Q) + C.
+// Loads go through per-lane addresses: the two halves of a wave may read
+// different tensors.
+template <uint32_t LANES>
+__device__ __forceinline__ void part_reduce(Lane& ln) {
+#pragma unroll
+  for (uint32_t off = LANES / 2; off > 0; off >>= 1) {  // stays within the LANES lanes
+    ln.s += __shfl_xor(ln.s, off);
+    ln.w += __shfl_xor(ln.w, off);
+    ln.x ^= __shfl_xor(ln.x, off);
+    ln.nf += __shfl_xor(ln.nf, off);
+  }
+}
+
+template <class Ty, uint32_t LANES>
 __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane& ln) {
   typedef Acc<Ty::ES, Ty::SIGNED, Ty::CHK> A_t;
   constexpr uint32_t es = Ty::ES;
@@ -280,18 +293,17 @@ __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane&
   const Span sp = span_of<es>(it);
   const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
   if (l < sp.h) scan_scalar<Ty>(sp.base + (uint64_t)l * es, l, rule, ln);
-  if (l >= 32u && l - 32u < sp.ntail) {
-    const uint32_t j = sp.tail0 + (l - 32u);
+  if (l >= LANES / 2 && l - LANES / 2 < sp.ntail) {
+    const uint32_t j = sp.tail0 + (l - LANES / 2);
     scan_scalar<Ty>(sp.base + (uint64_t)j * es, j, rule, ln);
   }
   if (sp.nvec) {
     const unsigned char* body = sp.base + (uint64_t)sp.h * es;
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(body, sp.nvec * kVecBytes);
     u32x4 v[kWaveVecs];
 #pragma unroll
     for (uint32_t u = 0; u < kWaveVecs; ++u) {
-      const uint32_t vi = u * 64u + l;
-      v[u] = (vi < sp.nvec) ? load16(rs, vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t vi = u * LANES + l;
+      v[u] = (vi < sp.nvec) ? load16_nt(body + (uint64_t)vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
     }
     A_t acc(rule);
 #pragma unroll
@@ -299,15 +311,16 @@ __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane&
     const uint64_t T = kWaveVecs;
     const uint64_t A = acc.sum();
     ln.s += A;
-    ln.w += (uint64_t)(sp.h + 1u + E * l) * A + (uint64_t)(64u * E) * (T * A - acc.q) + acc.csum();
+    ln.w += (uint64_t)(sp.h + 1u + E * l) * A + (uint64_t)(LANES * E) * (T * A - acc.q) + acc.csum();
     ln.x ^= acc.x;
     if (acc.chk.flagged()) {  // rare: reload this lane's vectors and count exactly
       uint32_t c = 0;
-      for (uint32_t vi = l; vi < sp.nvec; vi += 64u) c += nf_vec<es>(load16(rs, vi * kVecBytes), rule);
+      for (uint32_t vi = l; vi < sp.nvec; vi += LANES)
+        c += nf_vec<es>(load16_nt(body + (uint64_t)vi * kVecBytes), rule);
       ln.nf += c;
     }
   }
-  wave_reduce(ln);
+  part_reduce<LANES>(ln);
   ln.x = finish_xor<Ty>(ln.x);
 }
 

@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __res
   if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
 }
 
-template <class Ty>
+template <class Ty, uint32_t LANES>
 __device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t l) {
   constexpr uint32_t es = Ty::ES;
   uint32_t c = 0;
@@ -77,36 +77,35 @@ __device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t
     const Span sp = span_of<es>(it);
     const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
     if (l < sp.h) c += nf_exact(load_elem<es>(sp.base + (uint64_t)l * es), rule);
-    if (l >= 32u && l - 32u < sp.ntail)
-      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - 32u) * es), rule);
-    if (sp.nvec) {
-      __amdgpu_buffer_rsrc_t rs = make_rsrc(sp.base + (uint64_t)sp.h * es, sp.nvec * kVecBytes);
+    if (l >= LANES / 2 && l - LANES / 2 < sp.ntail)
+      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - LANES / 2) * es), rule);
+    const unsigned char* body = sp.base + (uint64_t)sp.h * es;
 #pragma unroll
-      for (uint32_t u = 0; u < kWaveVecs; ++u) {
-        const uint32_t vi = u * 64u + l;
-        if (vi < sp.nvec) c += nf_vec<es>(load16(rs, vi * kVecBytes), rule);
-      }
+    for (uint32_t u = 0; u < kWaveVecs; ++u) {
+      const uint32_t vi = u * LANES + l;
+      if (vi < sp.nvec) c += nf_vec<es>(load16_nt(body + (uint64_t)vi * kVecBytes), rule);
     }
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  for (uint32_t off = LANES / 2; off > 0; off >>= 1) c += __shfl_xor(c, off);
   return c;
 }
 
 __global__ void __launch_bounds__(kBlock) nonfinite_small_kernel(const PlanItem* __restrict__ items,
-                                                                 uint32_t n,
+                                                                 uint32_t n_full, uint32_t n_half,
+                                                                 uint32_t g_full,
                                                                  uint64_t* __restrict__ counts,
                                                                  uint64_t* __restrict__ total) {
-  const uint32_t i = wave_item_index();
-  if (i >= n) return;
-  const PlanItem it = items[i];
-  const uint32_t l = threadIdx.x & 63u;
-  uint32_t c = 0;
-  dispatch_type(it.dtype_flags & ~kItemSigned,
-                [&](auto ty) { c = nonfinite_small<typename Unsigned<decltype(ty)>::type>(it, l); });
-  if (l != 0) return;
-  if (counts) counts[it.row] = c;
-  if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
+  for_wave_item(n_full, n_half, g_full, [&](uint32_t i, uint32_t l, auto lanes) {
+    const PlanItem it = items[i];
+    uint32_t c = 0;
+    dispatch_type(it.dtype_flags & ~kItemSigned, [&](auto ty) {
+      c = nonfinite_small<typename Unsigned<decltype(ty)>::type, decltype(lanes)::value>(it, l);
+    });
+    if (l != 0) return;
+    if (counts) counts[it.row] = c;
+    if (c) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)c);
+  });
 }
 
 __global__ void __launch_bounds__(kBlock) merge_counts_kernel(const PlanSplit* __restrict__ split,
@@ -151,9 +150,11 @@ extern "C" int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info
   if (st) return st;
   const uint64_t n_block = h_info->n_items - h_info->n_small;
   if (h_info->n_small) {
-    hipLaunchKernelGGL(nonfinite_small_kernel,
-                       dim3((uint32_t)((h_info->n_small + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
-                       v.items + n_block, (uint32_t)h_info->n_small, d_counts, d_total);
+    uint32_t g_full;
+    const uint32_t g = wave_item_groups(h_info->n_small - h_info->n_half, h_info->n_half, &g_full);
+    hipLaunchKernelGGL(nonfinite_small_kernel, dim3(g), dim3(kBlock), 0, s, v.items + n_block,
+                       (uint32_t)(h_info->n_small - h_info->n_half), (uint32_t)h_info->n_half, g_full,
+                       d_counts, d_total);
     if ((st = launch_status())) return st;
   }
   if (n_block) {

@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(kBlock) sqnorm_kernel(const PlanItem* __restri
   else partials[it.slot].sum = (uint64_t)__double_as_longlong(acc);
 }
 
-template <class Dt>
+template <class Dt, uint32_t LANES>
 __device__ __forceinline__ double sq_small(const PlanItem& it, uint32_t l) {
   constexpr uint32_t DT = Dt::DTYPE, es = dt_size<DT>();
   const Span sp = span_of<es>(it);
@@ -155,31 +155,32 @@ __device__ __forceinline__ double sq_small(const PlanItem& it, uint32_t l) {
     const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)l * es));
     acc = y * y;
   }
-  if (l >= 32u && l - 32u < sp.ntail) {
-    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - 32u) * es));
+  if (l >= LANES / 2 && l - LANES / 2 < sp.ntail) {
+    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - LANES / 2) * es));
     acc = __builtin_fma(y, y, acc);
   }
-  if (sp.nvec) {
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(sp.base + (uint64_t)sp.h * es, sp.nvec * kVecBytes);
+  const unsigned char* body = sp.base + (uint64_t)sp.h * es;
 #pragma unroll
-    for (uint32_t u = 0; u < kWaveVecs; ++u) {
-      const uint32_t vi = u * 64u + l;
-      if (vi < sp.nvec) acc = sq_vec<DT>(load16(rs, vi * kVecBytes), acc);
-    }
+  for (uint32_t u = 0; u < kWaveVecs; ++u) {
+    const uint32_t vi = u * LANES + l;
+    if (vi < sp.nvec) acc = sq_vec<DT>(load16_nt(body + (uint64_t)vi * kVecBytes), acc);
   }
+#pragma unroll
+  for (uint32_t off = LANES / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   return acc;
 }
 
 __global__ void __launch_bounds__(kBlock) sqnorm_small_kernel(const PlanItem* __restrict__ items,
-                                                              uint32_t n, double* __restrict__ sq) {
-  const uint32_t i = wave_item_index();
-  if (i >= n) return;
-  const PlanItem it = items[i];
-  const uint32_t l = threadIdx.x & 63u;
-  double acc = 0.0;
-  dispatch_dtype(it.dtype_flags, [&](auto dt) { acc = sq_small<decltype(dt)>(it, l); });
-  acc = wave_sum_d(acc);
-  if (l == 0) sq[it.row] = acc;
+                                                              uint32_t n_full, uint32_t n_half,
+                                                              uint32_t g_full, double* __restrict__ sq) {
+  for_wave_item(n_full, n_half, g_full, [&](uint32_t i, uint32_t l, auto lanes) {
+    const PlanItem it = items[i];
+    double acc = 0.0;
+    dispatch_dtype(it.dtype_flags, [&](auto dt) {
+      acc = sq_small<decltype(dt), decltype(lanes)::value>(it, l);
+    });
+    if (l == 0) sq[it.row] = acc;
+  });
 }
 
 __global__ void __launch_bounds__(kBlock) merge_sq_kernel(const PlanSplit* __restrict__ split,
@@ -234,9 +235,11 @@ extern "C" int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, d
   const uint64_t n_block = h_info->n_items - h_info->n_small;
   int32_t st;
   if (h_info->n_small) {
-    hipLaunchKernelGGL(sqnorm_small_kernel,
-                       dim3((uint32_t)((h_info->n_small + kWaves - 1) / kWaves)), dim3(kBlock), 0, s,
-                       v.items + n_block, (uint32_t)h_info->n_small, d_sq);
+    uint32_t g_full;
+    const uint32_t g = wave_item_groups(h_info->n_small - h_info->n_half, h_info->n_half, &g_full);
+    hipLaunchKernelGGL(sqnorm_small_kernel, dim3(g), dim3(kBlock), 0, s, v.items + n_block,
+                       (uint32_t)(h_info->n_small - h_info->n_half), (uint32_t)h_info->n_half, g_full,
+                       d_sq);
     if ((st = launch_status())) return st;
   }
   if (n_block) {

@@ -60,18 +60,20 @@ __global__ void __launch_bounds__(kBlock) fingerprint_kernel(const PlanItem* __r
 }
 
 __global__ void __launch_bounds__(kBlock) fingerprint_small_kernel(const PlanItem* __restrict__ items,
-                                                                   uint32_t n,
+                                                                   uint32_t n_full, uint32_t n_half,
+                                                                   uint32_t g_full,
                                                                    sdc_row* __restrict__ out) {
-  const uint32_t i = wave_item_index();
-  if (i >= n) return;  // the whole wave leaves; no workgroup barrier in this kernel
-  const PlanItem it = items[i];
-  const uint32_t l = threadIdx.x & 63u;
-  Lane ln;
-  dispatch_type(it.dtype_flags, [&](auto ty) { scan_small<decltype(ty)>(it, l, ln); });
-  if (l != 0) return;
-  ulonglong2* d = reinterpret_cast<ulonglong2*>(out + it.row);
-  d[0] = ulonglong2{ln.s, ln.w};
-  d[1] = ulonglong2{ln.x, ln.nf};
+  for_wave_item(n_full, n_half, g_full, [&](uint32_t i, uint32_t l, auto lanes) {
+    const PlanItem it = items[i];
+    Lane ln;
+    dispatch_type(it.dtype_flags, [&](auto ty) {
+      scan_small<decltype(ty), decltype(lanes)::value>(it, l, ln);
+    });
+    if (l != 0) return;
+    ulonglong2* d = reinterpret_cast<ulonglong2*>(out + it.row);
+    d[0] = ulonglong2{ln.s, ln.w};
+    d[1] = ulonglong2{ln.x, ln.nf};
+  });
 }
 
 // Row of each split tensor from its items' partial rows: sums of S and of the
@@ -99,8 +101,10 @@ int32_t launch_scan(const void* d_plan, const sdc_plan_info* h, sdc_row* out, hi
   const uint64_t n_block = h->n_items - h->n_small;
   int32_t st;
   if (h->n_small) {
-    hipLaunchKernelGGL(fingerprint_small_kernel, dim3((uint32_t)((h->n_small + kWaves - 1) / kWaves)),
-                       dim3(kBlock), 0, s, v.items + n_block, (uint32_t)h->n_small, out);
+    uint32_t g_full;
+    const uint32_t g = wave_item_groups(h->n_small - h->n_half, h->n_half, &g_full);
+    hipLaunchKernelGGL(fingerprint_small_kernel, dim3(g), dim3(kBlock), 0, s, v.items + n_block,
+                       (uint32_t)(h->n_small - h->n_half), (uint32_t)h->n_half, g_full, out);
     if ((st = launch_status())) return st;
   }
   if (n_block) {

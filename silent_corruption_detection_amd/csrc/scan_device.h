@@ -5,6 +5,8 @@
 // wave index of wave items.
 #pragma once
 
+#include <type_traits>
+
 #include "sdc_internal.h"
 
 namespace sdc {
@@ -287,6 +289,40 @@ __device__ __forceinline__ uint64_t load_elem(const unsigned char* p) {
 // Index of the calling wave over the grid (4*block + wave), wave-uniform.
 __device__ __forceinline__ uint32_t wave_item_index() {
   return __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+}
+
+// The launch of a plan's wave items: workgroups [0, g_full) give each wave
+// one full-wave item, the others give each half wave one half-wave item
+// (full-wave items first in the plan).  Calls f(item, lane, lanes) for the
+// calling lane's item, lanes (64 or 32) as a compile-time constant; lanes
+// without an item do nothing.  No workgroup barrier may follow.
+constexpr uint32_t kFullPerBlock = kWaves;
+constexpr uint32_t kHalfPerBlock = kWaves * (64 / kHalfLanes);
+
+template <class F>
+__device__ __forceinline__ void for_wave_item(uint32_t n_full, uint32_t n_half, uint32_t g_full,
+                                              F&& f) {
+  if (blockIdx.x < g_full) {
+    const uint32_t i = wave_item_index();
+    if (i < n_full) f(i, threadIdx.x & 63u, std::integral_constant<uint32_t, 64>());
+  } else {
+    const uint32_t j = ((blockIdx.x - g_full) * kWaves + (threadIdx.x >> 6)) * (64 / kHalfLanes) +
+                       ((threadIdx.x & 63u) / kHalfLanes);
+    if (j < n_half)
+      f(n_full + j, threadIdx.x & (kHalfLanes - 1u), std::integral_constant<uint32_t, kHalfLanes>());
+  }
+}
+
+// Grid of that launch.
+inline uint32_t wave_item_groups(uint64_t n_full, uint64_t n_half, uint32_t* g_full) {
+  *g_full = (uint32_t)((n_full + kFullPerBlock - 1) / kFullPerBlock);
+  return *g_full + (uint32_t)((n_half + kHalfPerBlock - 1) / kHalfPerBlock);
+}
+
+// Non-temporal 16-byte load through a per-lane address (the two halves of a
+// wave read different tensors, so their base addresses are not uniform).
+__device__ __forceinline__ u32x4 load16_nt(const unsigned char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 // Head, aligned body and tail of an item of ES-byte elements.

@@ -43,7 +43,7 @@ def test_oracle_exports_every_declared_symbol():
 
 def test_status_and_version():
     import silent_corruption_detection_amd as sdc
-    assert sdc.sdc_abi_version() == 1
+    assert sdc.sdc_abi_version() == 2
     assert sdc.sdc_status_string(0) == "ok"
     for code in range(-7, 0):
         assert sdc.sdc_status_string(code) not in ("ok", "unknown status")
@@ -125,7 +125,8 @@ def one_tensor_plan_items(desc, item_bytes):
     class Info(ctypes.Structure):
         _fields_ = [(n, ctypes.c_uint64) for n in ("magic", "n_tensors", "n_items", "n_small",
                                                     "n_split", "n_slots", "total_elems",
-                                                    "total_bytes", "plan_bytes", "item_bytes")]
+                                                    "total_bytes", "plan_bytes", "item_bytes",
+                                                    "n_half")]
     info = Info()
     assert lib.sdc_plan_pack_host(arr, ctypes.c_uint64(1), ctypes.c_uint64(item_bytes), buf,
                                   ctypes.c_uint64(need.value), ctypes.byref(info)) == 0

@@ -13,7 +13,8 @@ import silent_corruption_detection_amd as sdc
 
 ES = {0: 4, 1: 2, 2: 2, 3: 8, 4: 1, 5: 1, 6: 1, 7: 1, 8: 1, 9: 2, 10: 4, 11: 8}
 WHOLE = 0x100
-WAVE_BODY_VECS = 512
+FULL_BODY_VECS = 512   # a wave item scanned by a whole wave: body <= 8 KiB
+HALF_BODY_VECS = 256   # by half a wave: body <= 4 KiB
 ITEM_MAX = 4 << 20
 
 
@@ -86,10 +87,14 @@ def check_plan(descs, item_bytes):
         whole = len(its) == 1
         for idx, x in its:
             assert bool(int(x["df"]) & WHOLE) == whole
-            if idx >= n_block:  # wave item: whole tensor with a short body
-                assert whole
-                h = 0 if ptr % 16 == 0 else min(numel, (16 - ptr % 16) // es)
-                assert (numel - h) * es // 16 <= WAVE_BODY_VECS
+            h = 0 if ptr % 16 == 0 else min(numel, (16 - ptr % 16) // es)
+            body = (numel - h) * es // 16
+            if idx >= info.n_items - info.n_half:    # half-wave item
+                assert whole and body <= HALF_BODY_VECS
+            elif idx >= n_block:                     # full-wave item
+                assert whole and HALF_BODY_VECS < body <= FULL_BODY_VECS
+            elif whole:                              # workgroup item of a whole tensor
+                assert body > FULL_BODY_VECS
     assert total == info.total_bytes
     # split table: missing/empty tensors (count 0) and multi-item tensors
     srows = {int(r[0]): (int(r[1]), int(r[2])) for r in split}
@@ -133,20 +138,44 @@ def test_random_lists_are_covered_exactly(item_bytes):
     assert info.n_items > 0
 
 
-def test_wave_items_and_block_items_split_at_8k():
+def test_wave_item_classes():
+    # aligned body <= 256 vectors (4 KiB): half a wave; <= 512 (8 KiB): a wave
     base = 0x7F0000000000
-    descs = [(base, 4096, 1, 0),          # 8 KiB bf16 aligned: a wave item
-             (base + 2, 4096, 1, 0),      # misaligned: head 7, body 4089 -> 511 vectors + tail
-             (base + 16, 4104, 1, 0),     # 513 vectors: a workgroup item
-             (base, 2048, 0, 0),          # 8 KiB fp32
-             (base, 2049, 0, 0),          # 512 vectors + a 1-element tail
-             (base, 2052, 0, 0),          # 513 vectors: a workgroup item
-             (base, 1, 2, 0)]
+    descs = [(base, 2048, 1, 0),          # 4 KiB bf16 aligned: half wave
+             (base + 2, 2048, 1, 0),      # misaligned: head 7, body 2041 -> 255 vectors + tail
+             (base + 16, 2056, 1, 0),     # 257 vectors: a wave
+             (base, 1024, 0, 0),          # 4 KiB fp32: half wave
+             (base, 1025, 0, 0),          # 256 vectors + a 1-element tail: half wave
+             (base, 1028, 0, 0),          # 257 vectors: a wave
+             (base, 1, 2, 0),             # half wave
+             (base, 4096, 1, 0),          # 8 KiB: a wave
+             (base, 4104, 1, 0),          # 513 vectors: a workgroup item
+             (base, 2049, 0, 0)]          # 512 vectors + tail: a wave
     img, info, _ = pack(descs, 0)
     _, items, _ = parse(img, info)
     n_block = info.n_items - info.n_small
-    wave_rows = sorted(int(x["row"]) for x in items[n_block:])
-    assert wave_rows == [0, 1, 3, 4, 6]
+    n_full = info.n_small - info.n_half
+    full_rows = sorted(int(x["row"]) for x in items[n_block:n_block + n_full])
+    half_rows = sorted(int(x["row"]) for x in items[n_block + n_full:])
+    assert half_rows == [0, 1, 3, 4, 6]
+    assert full_rows == [2, 5, 7, 9]
+    check_plan(descs, 0)
+
+
+def test_wave_items_are_grouped_by_type():
+    # each class of wave items is stored grouped by element type (stable within a type)
+    base = 0x7F0000000000
+    dts = [0, 1, 2, 1, 0, 2, 2, 1, 0, 0]
+    sizes = [100, 3000, 3000, 100, 1500, 100, 3000, 100, 1500, 100]   # half / full classes
+    descs = [(base + (1 << 16) * k, n, dt, 0) for k, (dt, n) in enumerate(zip(dts, sizes))]
+    img, info, _ = pack(descs, 0)
+    _, items, _ = parse(img, info)
+    n_block = info.n_items - info.n_small
+    n_full = info.n_small - info.n_half
+    for lo, hi in ((n_block, n_block + n_full), (n_block + n_full, info.n_items)):
+        got = [(int(x["df"]) & 0xFF, int(x["row"])) for x in items[lo:hi]]
+        assert got == sorted(got)
+    assert n_full == 5 and info.n_half == 5
     check_plan(descs, 0)
 
 
