@@ -117,15 +117,15 @@ typedef struct {
   uint64_t magic;        /* identifies a plan built by sdc_plan_build            */
   uint64_t n_tensors;    /* number of descriptors = number of output rows        */
   uint64_t n_items;      /* work items (workgroup items + wave items)            */
-  uint64_t n_small;      /* of which wave items: small tensors scanned by a wave
-                            or half a wave                                     */
+  uint64_t n_small;      /* of which wave items: small tensors scanned whole by
+                            a group of lanes of one wave                        */
   uint64_t n_split;      /* rows merged from several items (or missing/empty)    */
   uint64_t n_slots;      /* partial-row slots in the plan's scratch area         */
   uint64_t total_elems;  /* elements scanned per pass                            */
   uint64_t total_bytes;  /* bytes scanned per pass (the algorithmic traffic)     */
   uint64_t plan_bytes;   /* bytes of the device plan                             */
   uint64_t item_bytes;   /* bytes per work item (the chunk size used)            */
-  uint64_t n_half;       /* of the wave items, those scanned by half a wave       */
+  uint64_t n_wave[4];    /* wave items by class: scanned by 64, 32, 16, 8 lanes   */
 } sdc_plan_info;
 
 /* Result of sdc_majority_compare ([BLOG] "Check 3"). */
@@ -174,9 +174,9 @@ int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_by
  * header {magic, n_tensors, n_items, n_split, n_slots, total_bytes,
  * item_bytes, n_small} (uint64 each); n_items 32-byte work items {addr u64,
  * start u64, len u32, row u32, slot u32, dtype | 0x100 if whole-tensor u32},
- * workgroup items first, then the n_small wave items (n_small - n_half
- * full-wave items, then n_half half-wave items, each group ordered by element
- * type); then n_split 16-byte
+ * workgroup items first, then the n_small wave items (the n_wave[0..3] items
+ * of each class in turn, each class ordered by element type); then n_split
+ * 16-byte
  * entries {row, first slot, slot count, 0} (uint32 each). */
 int32_t sdc_plan_pack_host(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
                            void* h_plan, uint64_t plan_bytes, sdc_plan_info* h_info);

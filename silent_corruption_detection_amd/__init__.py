@@ -51,7 +51,7 @@ class _Tensor(ctypes.Structure):
 class _PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
                 ("magic", "n_tensors", "n_items", "n_small", "n_split", "n_slots", "total_elems",
-                 "total_bytes", "plan_bytes", "item_bytes", "n_half")]
+                 "total_bytes", "plan_bytes", "item_bytes")] + [("n_wave", ctypes.c_uint64 * 4)]
 
 
 class _Majority(ctypes.Structure):

@@ -268,7 +268,7 @@ __device__ __forceinline__ void scan_item(const PlanItem& it, Lane& ln) {
   ln.x = finish_xor<Ty>(ln.x);
 }
 
-// ---- wave items: small tensors, one wave or half a wave each --------------------
+// ---- wave items: small tensors, one group of lanes each ---------------------------
 // The aligned body has at most LANES x kWaveVecs vectors; lane l loads vectors
 // LANES*u + l for u = 0 .. kWaveVecs-1 all at once (T = kWaveVecs, missing
 // vectors count as zero), then W_lane = (h+1+E*l)*A + LANES*E*(T*A - Q) + C.
@@ -292,11 +292,9 @@ __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane&
   constexpr uint32_t E = kVecBytes / es;
   const Span sp = span_of<es>(it);
   const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
-  if (l < sp.h) scan_scalar<Ty>(sp.base + (uint64_t)l * es, l, rule, ln);
-  if (l >= LANES / 2 && l - LANES / 2 < sp.ntail) {
-    const uint32_t j = sp.tail0 + (l - LANES / 2);
+  for_head_tail<LANES>(sp, l, [&](uint32_t j) {
     scan_scalar<Ty>(sp.base + (uint64_t)j * es, j, rule, ln);
-  }
+  });
   if (sp.nvec) {
     const unsigned char* body = sp.base + (uint64_t)sp.h * es;
     u32x4 v[kWaveVecs];

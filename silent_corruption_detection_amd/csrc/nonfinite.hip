@@ -76,9 +76,9 @@ __device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t
   if constexpr (Ty::CHK != kChkNone) {
     const Span sp = span_of<es>(it);
     const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
-    if (l < sp.h) c += nf_exact(load_elem<es>(sp.base + (uint64_t)l * es), rule);
-    if (l >= LANES / 2 && l - LANES / 2 < sp.ntail)
-      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - LANES / 2) * es), rule);
+    for_head_tail<LANES>(sp, l, [&](uint32_t j) {
+      c += nf_exact(load_elem<es>(sp.base + (uint64_t)j * es), rule);
+    });
     const unsigned char* body = sp.base + (uint64_t)sp.h * es;
 #pragma unroll
     for (uint32_t u = 0; u < kWaveVecs; ++u) {
@@ -92,11 +92,10 @@ __device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t
 }
 
 __global__ void __launch_bounds__(kBlock) nonfinite_small_kernel(const PlanItem* __restrict__ items,
-                                                                 uint32_t n_full, uint32_t n_half,
-                                                                 uint32_t g_full,
+                                                                 WaveLaunch w,
                                                                  uint64_t* __restrict__ counts,
                                                                  uint64_t* __restrict__ total) {
-  for_wave_item(n_full, n_half, g_full, [&](uint32_t i, uint32_t l, auto lanes) {
+  for_wave_item(w, [&](uint32_t i, uint32_t l, auto lanes) {
     const PlanItem it = items[i];
     uint32_t c = 0;
     dispatch_type(it.dtype_flags & ~kItemSigned, [&](auto ty) {
@@ -150,11 +149,9 @@ extern "C" int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info
   if (st) return st;
   const uint64_t n_block = h_info->n_items - h_info->n_small;
   if (h_info->n_small) {
-    uint32_t g_full;
-    const uint32_t g = wave_item_groups(h_info->n_small - h_info->n_half, h_info->n_half, &g_full);
-    hipLaunchKernelGGL(nonfinite_small_kernel, dim3(g), dim3(kBlock), 0, s, v.items + n_block,
-                       (uint32_t)(h_info->n_small - h_info->n_half), (uint32_t)h_info->n_half, g_full,
-                       d_counts, d_total);
+    const WaveLaunch w = wave_launch(h_info->n_wave);
+    hipLaunchKernelGGL(nonfinite_small_kernel, dim3(w.group[kWaveClasses]), dim3(kBlock), 0, s,
+                       v.items + n_block, w, d_counts, d_total);
     if ((st = launch_status())) return st;
   }
   if (n_block) {

@@ -151,14 +151,10 @@ __device__ __forceinline__ double sq_small(const PlanItem& it, uint32_t l) {
   constexpr uint32_t DT = Dt::DTYPE, es = dt_size<DT>();
   const Span sp = span_of<es>(it);
   double acc = 0.0;
-  if (l < sp.h) {
-    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)l * es));
-    acc = y * y;
-  }
-  if (l >= LANES / 2 && l - LANES / 2 < sp.ntail) {
-    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + l - LANES / 2) * es));
+  for_head_tail<LANES>(sp, l, [&](uint32_t j) {
+    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)j * es));
     acc = __builtin_fma(y, y, acc);
-  }
+  });
   const unsigned char* body = sp.base + (uint64_t)sp.h * es;
 #pragma unroll
   for (uint32_t u = 0; u < kWaveVecs; ++u) {
@@ -171,9 +167,8 @@ __device__ __forceinline__ double sq_small(const PlanItem& it, uint32_t l) {
 }
 
 __global__ void __launch_bounds__(kBlock) sqnorm_small_kernel(const PlanItem* __restrict__ items,
-                                                              uint32_t n_full, uint32_t n_half,
-                                                              uint32_t g_full, double* __restrict__ sq) {
-  for_wave_item(n_full, n_half, g_full, [&](uint32_t i, uint32_t l, auto lanes) {
+                                                              WaveLaunch w, double* __restrict__ sq) {
+  for_wave_item(w, [&](uint32_t i, uint32_t l, auto lanes) {
     const PlanItem it = items[i];
     double acc = 0.0;
     dispatch_dtype(it.dtype_flags, [&](auto dt) {
@@ -235,11 +230,9 @@ extern "C" int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, d
   const uint64_t n_block = h_info->n_items - h_info->n_small;
   int32_t st;
   if (h_info->n_small) {
-    uint32_t g_full;
-    const uint32_t g = wave_item_groups(h_info->n_small - h_info->n_half, h_info->n_half, &g_full);
-    hipLaunchKernelGGL(sqnorm_small_kernel, dim3(g), dim3(kBlock), 0, s, v.items + n_block,
-                       (uint32_t)(h_info->n_small - h_info->n_half), (uint32_t)h_info->n_half, g_full,
-                       d_sq);
+    const WaveLaunch w = wave_launch(h_info->n_wave);
+    hipLaunchKernelGGL(sqnorm_small_kernel, dim3(w.group[kWaveClasses]), dim3(kBlock), 0, s,
+                       v.items + n_block, w, d_sq);
     if ((st = launch_status())) return st;
   }
   if (n_block) {

@@ -12,8 +12,8 @@ namespace {
 
 // ---- host side: plan layout --------------------------------------------------
 struct Layout {
-  uint64_t n_items = 0, n_small = 0, n_half = 0, n_split = 0, n_slots = 0, total_elems = 0;
-  uint64_t total_bytes = 0;
+  uint64_t n_items = 0, n_small = 0, n_split = 0, n_slots = 0, total_elems = 0, total_bytes = 0;
+  uint64_t n_wave[kWaveClasses] = {0, 0, 0, 0};
   uint64_t item_bytes = 0;
   PlanOffsets off{};
 };
@@ -42,17 +42,20 @@ uint64_t items_of(uint64_t ptr, uint64_t numel, uint32_t es, uint64_t item_bytes
 
 bool has_data(const sdc_tensor& t) { return t.ptr != nullptr && t.numel != 0; }
 
-// Wave-item class of a tensor: 0 = workgroup item(s), 1 = scanned whole by a
-// wave, 2 = by half a wave.  A wave item is a single item anyway, and its
-// aligned body fits the lanes' kWaveVecs vectors each.
-enum : int { kClassBlock = 0, kClassFull = 1, kClassHalf = 2 };
+// Wave-item class of a tensor: -1 = workgroup item(s); c = 0..3 = scanned
+// whole by 64 >> c lanes.  A wave item is a single item anyway, and its
+// aligned body fits the group's kWaveVecs vectors per lane (the narrowest
+// group that fits).
+constexpr int kClassBlock = -1;
 
 int wave_class(uint64_t ptr, uint64_t numel, uint32_t es, uint64_t item_bytes) {
   if (items_of(ptr, numel, es, item_bytes) != 1) return kClassBlock;
   const uint64_t mis = ptr & 15u;
   const uint64_t h = mis ? std::min<uint64_t>(numel, (16u - mis) / es) : 0u;
   const uint64_t body = (numel - h) * es / kVecBytes;
-  return body <= kHalfBodyVecs ? kClassHalf : body <= kFullBodyVecs ? kClassFull : kClassBlock;
+  for (int c = kWaveClasses - 1; c >= 0; --c)
+    if (body <= class_body_vecs((uint32_t)c)) return c;
+  return kClassBlock;
 }
 
 int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout* L) {
@@ -71,7 +74,8 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
     bytes += t[k].numel * es;
   }
   if (item_bytes == 0) item_bytes = auto_item_bytes(bytes);
-  uint64_t items = 0, small = 0, half = 0, split = 0, slots = 0;
+  uint64_t items = 0, small = 0, split = 0, slots = 0;
+  uint64_t nw[kWaveClasses] = {0, 0, 0, 0};
   for (uint64_t k = 0; k < n; ++k) {
     if (!has_data(t[k])) {
       split++;
@@ -82,8 +86,10 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
     const uint64_t c = items_of(ptr, t[k].numel, es, item_bytes);
     items += c;
     const int wc = wave_class(ptr, t[k].numel, es, item_bytes);
-    small += wc != kClassBlock;
-    half += wc == kClassHalf;
+    if (wc != kClassBlock) {
+      small++;
+      nw[wc]++;
+    }
     if (c > 1) {
       split++;
       slots += c;
@@ -92,7 +98,7 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
   if (items > kMaxGrid || slots >= (1ull << 32)) return SDC_ERR_RANGE;
   L->n_items = items;
   L->n_small = small;
-  L->n_half = half;
+  for (uint32_t c = 0; c < kWaveClasses; ++c) L->n_wave[c] = nw[c];
   L->n_split = split;
   L->n_slots = slots;
   L->total_elems = elems;
@@ -118,7 +124,12 @@ void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<uns
   hd->n_small = L.n_small;
   PlanItem* items = reinterpret_cast<PlanItem*>(img.data() + L.off.items);
   PlanSplit* split = reinterpret_cast<PlanSplit*>(img.data() + L.off.split);
-  uint64_t ni = 0, nw = L.n_items - L.n_small, nh = L.n_items - L.n_half, ns = 0, slot = 0;
+  // next free index of the workgroup items and of each wave-item class
+  uint64_t ni = 0, ns = 0, slot = 0;
+  uint64_t wi[kWaveClasses + 1];
+  wi[0] = L.n_items - L.n_small;
+  for (uint32_t c = 0; c < kWaveClasses; ++c) wi[c + 1] = wi[c] + L.n_wave[c];
+  const uint64_t class_start[kWaveClasses + 1] = {wi[0], wi[1], wi[2], wi[3], wi[4]};
   for (uint64_t k = 0; k < n; ++k) {
     if (!has_data(t[k])) {
       split[ns++] = PlanSplit{(uint32_t)k, 0u, 0u, 0u};
@@ -131,7 +142,7 @@ void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<uns
     const int wc = wave_class(ptr, t[k].numel, es, L.item_bytes);
     if (c > 1) split[ns++] = PlanSplit{(uint32_t)k, (uint32_t)slot, (uint32_t)c, 0u};
     split_tensor(ptr, t[k].numel, es, L.item_bytes, [&](uint64_t s, uint64_t len) {
-      PlanItem& it = items[wc == kClassHalf ? nh++ : wc == kClassFull ? nw++ : ni++];
+      PlanItem& it = items[wc == kClassBlock ? ni++ : wi[wc]++];
       it.addr = ptr + s * es;
       it.start = s;
       it.len = (uint32_t)len;
@@ -147,8 +158,8 @@ void pack_plan(const sdc_tensor* t, uint64_t n, const Layout& L, std::vector<uns
     return (a.dtype_flags & (kItemDtypeMask | kItemSigned)) <
            (b.dtype_flags & (kItemDtypeMask | kItemSigned));
   };
-  std::stable_sort(items + (L.n_items - L.n_small), items + (L.n_items - L.n_half), by_type);
-  std::stable_sort(items + (L.n_items - L.n_half), items + L.n_items, by_type);
+  for (uint32_t c = 0; c < kWaveClasses; ++c)
+    std::stable_sort(items + class_start[c], items + class_start[c + 1], by_type);
 }
 
 }  // namespace
@@ -189,7 +200,7 @@ extern "C" int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint6
   h_info->n_tensors = n;
   h_info->n_items = L.n_items;
   h_info->n_small = L.n_small;
-  h_info->n_half = L.n_half;
+  for (uint32_t c = 0; c < kWaveClasses; ++c) h_info->n_wave[c] = L.n_wave[c];
   h_info->n_split = L.n_split;
   h_info->n_slots = L.n_slots;
   h_info->total_elems = L.total_elems;
@@ -217,7 +228,7 @@ extern "C" int32_t sdc_plan_pack_host(const sdc_tensor* h_tensors, uint64_t n, u
   h_info->n_tensors = n;
   h_info->n_items = L.n_items;
   h_info->n_small = L.n_small;
-  h_info->n_half = L.n_half;
+  for (uint32_t c = 0; c < kWaveClasses; ++c) h_info->n_wave[c] = L.n_wave[c];
   h_info->n_split = L.n_split;
   h_info->n_slots = L.n_slots;
   h_info->total_elems = L.total_elems;

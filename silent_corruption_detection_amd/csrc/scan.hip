@@ -60,10 +60,9 @@ __global__ void __launch_bounds__(kBlock) fingerprint_kernel(const PlanItem* __r
 }
 
 __global__ void __launch_bounds__(kBlock) fingerprint_small_kernel(const PlanItem* __restrict__ items,
-                                                                   uint32_t n_full, uint32_t n_half,
-                                                                   uint32_t g_full,
+                                                                   WaveLaunch w,
                                                                    sdc_row* __restrict__ out) {
-  for_wave_item(n_full, n_half, g_full, [&](uint32_t i, uint32_t l, auto lanes) {
+  for_wave_item(w, [&](uint32_t i, uint32_t l, auto lanes) {
     const PlanItem it = items[i];
     Lane ln;
     dispatch_type(it.dtype_flags, [&](auto ty) {
@@ -101,10 +100,9 @@ int32_t launch_scan(const void* d_plan, const sdc_plan_info* h, sdc_row* out, hi
   const uint64_t n_block = h->n_items - h->n_small;
   int32_t st;
   if (h->n_small) {
-    uint32_t g_full;
-    const uint32_t g = wave_item_groups(h->n_small - h->n_half, h->n_half, &g_full);
-    hipLaunchKernelGGL(fingerprint_small_kernel, dim3(g), dim3(kBlock), 0, s, v.items + n_block,
-                       (uint32_t)(h->n_small - h->n_half), (uint32_t)h->n_half, g_full, out);
+    const WaveLaunch w = wave_launch(h->n_wave);
+    hipLaunchKernelGGL(fingerprint_small_kernel, dim3(w.group[kWaveClasses]), dim3(kBlock), 0, s,
+                       v.items + n_block, w, out);
     if ((st = launch_status())) return st;
   }
   if (n_block) {

@@ -291,32 +291,45 @@ __device__ __forceinline__ uint32_t wave_item_index() {
   return __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
 }
 
-// The launch of a plan's wave items: workgroups [0, g_full) give each wave
-// one full-wave item, the others give each half wave one half-wave item
-// (full-wave items first in the plan).  Calls f(item, lane, lanes) for the
-// calling lane's item, lanes (64 or 32) as a compile-time constant; lanes
-// without an item do nothing.  No workgroup barrier may follow.
-constexpr uint32_t kFullPerBlock = kWaves;
-constexpr uint32_t kHalfPerBlock = kWaves * (64 / kHalfLanes);
+// The launch of a plan's wave items.  Class c's items (1 << c per wave,
+// 4 << c per workgroup) take workgroups [group[c], group[c+1]); their indices
+// among the wave items start at first[c].
+struct WaveLaunch {
+  uint32_t first[kWaveClasses], count[kWaveClasses], group[kWaveClasses + 1];
+};
 
-template <class F>
-__device__ __forceinline__ void for_wave_item(uint32_t n_full, uint32_t n_half, uint32_t g_full,
-                                              F&& f) {
-  if (blockIdx.x < g_full) {
-    const uint32_t i = wave_item_index();
-    if (i < n_full) f(i, threadIdx.x & 63u, std::integral_constant<uint32_t, 64>());
-  } else {
-    const uint32_t j = ((blockIdx.x - g_full) * kWaves + (threadIdx.x >> 6)) * (64 / kHalfLanes) +
-                       ((threadIdx.x & 63u) / kHalfLanes);
-    if (j < n_half)
-      f(n_full + j, threadIdx.x & (kHalfLanes - 1u), std::integral_constant<uint32_t, kHalfLanes>());
+inline WaveLaunch wave_launch(const uint64_t* n_wave) {
+  WaveLaunch w;
+  uint64_t first = 0, group = 0;
+  for (uint32_t c = 0; c < kWaveClasses; ++c) {
+    w.first[c] = (uint32_t)first;
+    w.count[c] = (uint32_t)n_wave[c];
+    w.group[c] = (uint32_t)group;
+    first += n_wave[c];
+    group += (n_wave[c] + (kWaves << c) - 1) / (kWaves << c);
   }
+  w.group[kWaveClasses] = (uint32_t)group;
+  return w;
 }
 
-// Grid of that launch.
-inline uint32_t wave_item_groups(uint64_t n_full, uint64_t n_half, uint32_t* g_full) {
-  *g_full = (uint32_t)((n_full + kFullPerBlock - 1) / kFullPerBlock);
-  return *g_full + (uint32_t)((n_half + kHalfPerBlock - 1) / kHalfPerBlock);
+template <uint32_t C, class F>
+__device__ __forceinline__ void run_wave_class(const WaveLaunch& w, F& f) {
+  constexpr uint32_t kLanes = class_lanes(C);
+  const uint32_t j = ((blockIdx.x - w.group[C]) * kWaves + (threadIdx.x >> 6)) * (1u << C) +
+                     ((threadIdx.x & 63u) / kLanes);
+  if (j < w.count[C])
+    f(w.first[C] + j, threadIdx.x & (kLanes - 1u), std::integral_constant<uint32_t, kLanes>());
+}
+
+// Calls f(item, lane, lanes) for the calling lane's wave item, lanes (the
+// group width) as a compile-time constant; lanes without an item do nothing.
+// The class is uniform over a workgroup.  No workgroup barrier may follow.
+template <class F>
+__device__ __forceinline__ void for_wave_item(const WaveLaunch& w, F&& f) {
+  if (blockIdx.x < w.group[1]) run_wave_class<0>(w, f);
+  else if (blockIdx.x < w.group[2]) run_wave_class<1>(w, f);
+  else if (blockIdx.x < w.group[3]) run_wave_class<2>(w, f);
+  else run_wave_class<3>(w, f);
 }
 
 // Non-temporal 16-byte load through a per-lane address (the two halves of a
@@ -342,6 +355,19 @@ __device__ __forceinline__ Span span_of(const PlanItem& it) {
   sp.tail0 = sp.h + sp.nvec * (kVecBytes / ES);
   sp.ntail = len - sp.tail0;
   return sp;
+}
+
+// Head and tail elements of a wave item (fewer than 16 each), given out to
+// the LANES lanes of its group: f(j) with j the element's index in the item.
+template <uint32_t LANES, class F>
+__device__ __forceinline__ void for_head_tail(const Span& sp, uint32_t l, F&& f) {
+  if constexpr (LANES >= 32) {  // head on the first lanes, tail on the upper half
+    if (l < sp.h) f(l);
+    if (l >= LANES / 2 && l - LANES / 2 < sp.ntail) f(sp.tail0 + (l - LANES / 2));
+  } else {
+    for (uint32_t j = l; j < sp.h; j += LANES) f(j);
+    for (uint32_t j = l; j < sp.ntail; j += LANES) f(sp.tail0 + j);
+  }
 }
 
 }  // namespace

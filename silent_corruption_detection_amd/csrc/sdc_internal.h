@@ -47,16 +47,16 @@ inline uint64_t tensor_item_bytes(uint64_t bytes) {
 
 constexpr uint64_t kPlanMagic = 0x31766E6163534453ull;  // "SDScanv1", little-endian
 
-// Wave items: small tensors scanned whole by part of a wave, kWaveVecs
-// vectors per lane, every load of a lane issued at once, and a reduction
-// within that part.  A body of at most 32 x 8 vectors (4 KiB) takes half a
-// wave (two tensors per wave: small tensors are latency-bound, so this doubles
-// the loads in flight at the same register cost); a body of at most 64 x 8
-// vectors (8 KiB) takes a whole wave.
+// Wave items: small tensors scanned whole by a group of 64 >> c lanes of a
+// wave (class c = 0..3: 64, 32, 16 or 8 lanes), kWaveVecs vectors per lane,
+// every load of a lane issued at once, and a reduction within the group.
+// Class c takes bodies of at most (64 >> c) x 8 vectors (8, 4, 2, 1 KiB) and
+// puts 1 << c tensors in a wave: small tensors are latency-bound, so narrower
+// groups keep more loads in flight at the same register cost.
 constexpr uint32_t kWaveVecs = 8;
-constexpr uint32_t kHalfLanes = 32;
-constexpr uint32_t kFullBodyVecs = 64 * kWaveVecs;
-constexpr uint32_t kHalfBodyVecs = kHalfLanes * kWaveVecs;
+constexpr uint32_t kWaveClasses = 4;
+constexpr uint32_t class_lanes(uint32_t c) { return 64u >> c; }
+constexpr uint32_t class_body_vecs(uint32_t c) { return class_lanes(c) * kWaveVecs; }
 
 // Item flags: the item is the whole tensor, so it stores the tensor's row;
 // the tensor's 2-/4-byte patterns are sign-extended (SDC_FLAG_SIGNED).
@@ -67,8 +67,8 @@ constexpr uint32_t kItemDtypeMask = 0xFFu;
 // Device plan, all offsets from the plan's base:
 //   [PlanHeader]
 //   [PlanItem   x n_items]   n_items - n_small workgroup items, then the
-//                            n_small - n_half full-wave items, then the
-//                            n_half half-wave items
+//                            n_small wave items, class 0 to 3 (n_wave[c]
+//                            each)
 //   [PlanSplit  x n_split]   tensors not covered by exactly one item
 //   (pad to 256)
 //   [sdc_row    x n_slots]   partial rows of the items of split tensors
@@ -149,8 +149,11 @@ inline hipStream_t as_stream(sdc_stream_t s) { return reinterpret_cast<hipStream
 // image's parts.
 inline bool info_ok(const sdc_plan_info* h) {
   if (h == nullptr || h->magic != kPlanMagic || h->n_items > kMaxGrid ||
-      h->n_split > h->n_tensors || h->n_small > h->n_items || h->n_half > h->n_small)
+      h->n_split > h->n_tensors || h->n_small > h->n_items)
     return false;
+  uint64_t w = 0;
+  for (uint32_t c = 0; c < kWaveClasses; ++c) w += h->n_wave[c];
+  if (w != h->n_small) return false;
   return h->plan_bytes >= plan_offsets(h->n_items, h->n_split, h->n_slots).end;
 }
 

@@ -125,8 +125,8 @@ def one_tensor_plan_items(desc, item_bytes):
     class Info(ctypes.Structure):
         _fields_ = [(n, ctypes.c_uint64) for n in ("magic", "n_tensors", "n_items", "n_small",
                                                     "n_split", "n_slots", "total_elems",
-                                                    "total_bytes", "plan_bytes", "item_bytes",
-                                                    "n_half")]
+                                                    "total_bytes", "plan_bytes", "item_bytes")
+                    ] + [("n_wave", ctypes.c_uint64 * 4)]
     info = Info()
     assert lib.sdc_plan_pack_host(arr, ctypes.c_uint64(1), ctypes.c_uint64(item_bytes), buf,
                                   ctypes.c_uint64(need.value), ctypes.byref(info)) == 0

@@ -13,8 +13,8 @@ import silent_corruption_detection_amd as sdc
 
 ES = {0: 4, 1: 2, 2: 2, 3: 8, 4: 1, 5: 1, 6: 1, 7: 1, 8: 1, 9: 2, 10: 4, 11: 8}
 WHOLE = 0x100
-FULL_BODY_VECS = 512   # a wave item scanned by a whole wave: body <= 8 KiB
-HALF_BODY_VECS = 256   # by half a wave: body <= 4 KiB
+# wave items of class c are scanned by 64 >> c lanes: aligned body <= 512 >> c vectors
+CLASS_BODY_VECS = [512, 256, 128, 64]
 ITEM_MAX = 4 << 20
 
 
@@ -48,12 +48,23 @@ def parse(img, info):
     return hdr, items, split
 
 
+def class_of(info, idx):
+    """Wave-item class of plan item idx (items of class 0..3 follow the workgroup items)."""
+    start = info.n_items - info.n_small
+    for c in range(4):
+        start += info.n_wave[c]
+        if idx < start:
+            return c
+    raise AssertionError("not a wave item")
+
+
 def check_plan(descs, item_bytes):
     img, info, nbytes = pack(descs, item_bytes)
     hdr, items, split = parse(img, info)
     assert int(hdr[1]) == len(descs) == info.n_tensors
     assert int(hdr[2]) == info.n_items and int(hdr[3]) == info.n_split
     assert int(hdr[4]) == info.n_slots and int(hdr[7]) == info.n_small
+    assert sum(info.n_wave) == info.n_small
     assert info.plan_bytes == nbytes
     ib = info.item_bytes
     assert ib % 16 == 0 and 16 <= ib <= ITEM_MAX
@@ -89,12 +100,13 @@ def check_plan(descs, item_bytes):
             assert bool(int(x["df"]) & WHOLE) == whole
             h = 0 if ptr % 16 == 0 else min(numel, (16 - ptr % 16) // es)
             body = (numel - h) * es // 16
-            if idx >= info.n_items - info.n_half:    # half-wave item
-                assert whole and body <= HALF_BODY_VECS
-            elif idx >= n_block:                     # full-wave item
-                assert whole and HALF_BODY_VECS < body <= FULL_BODY_VECS
+            if idx >= n_block:                       # wave item: the narrowest class that fits
+                assert whole
+                c = class_of(info, idx)
+                assert body <= CLASS_BODY_VECS[c]
+                assert c == 3 or body > CLASS_BODY_VECS[c + 1]
             elif whole:                              # workgroup item of a whole tensor
-                assert body > FULL_BODY_VECS
+                assert body > CLASS_BODY_VECS[0]
     assert total == info.total_bytes
     # split table: missing/empty tensors (count 0) and multi-item tensors
     srows = {int(r[0]): (int(r[1]), int(r[2])) for r in split}
@@ -139,26 +151,29 @@ def test_random_lists_are_covered_exactly(item_bytes):
 
 
 def test_wave_item_classes():
-    # aligned body <= 256 vectors (4 KiB): half a wave; <= 512 (8 KiB): a wave
+    # aligned body <= 64 vectors (1 KiB): 8 lanes; <= 128: 16; <= 256: 32; <= 512 (8 KiB): 64
     base = 0x7F0000000000
-    descs = [(base, 2048, 1, 0),          # 4 KiB bf16 aligned: half wave
-             (base + 2, 2048, 1, 0),      # misaligned: head 7, body 2041 -> 255 vectors + tail
-             (base + 16, 2056, 1, 0),     # 257 vectors: a wave
-             (base, 1024, 0, 0),          # 4 KiB fp32: half wave
-             (base, 1025, 0, 0),          # 256 vectors + a 1-element tail: half wave
-             (base, 1028, 0, 0),          # 257 vectors: a wave
-             (base, 1, 2, 0),             # half wave
-             (base, 4096, 1, 0),          # 8 KiB: a wave
+    descs = [(base, 2048, 1, 0),          # 4 KiB bf16 aligned: 256 vectors, class 1
+             (base + 2, 2048, 1, 0),      # misaligned: head 7, body 2041 -> 255 vectors + tail: 1
+             (base + 16, 2056, 1, 0),     # 257 vectors: class 0
+             (base, 1024, 0, 0),          # 4 KiB fp32: class 1
+             (base, 1025, 0, 0),          # 256 vectors + a 1-element tail: class 1
+             (base, 1028, 0, 0),          # 257 vectors: class 0
+             (base, 1, 2, 0),             # no body: class 3
+             (base, 4096, 1, 0),          # 8 KiB: class 0
              (base, 4104, 1, 0),          # 513 vectors: a workgroup item
-             (base, 2049, 0, 0)]          # 512 vectors + tail: a wave
+             (base, 2049, 0, 0),          # 512 vectors + tail: class 0
+             (base, 256, 0, 0),           # 64 vectors: class 3
+             (base, 257, 0, 0),           # 64 vectors + tail: class 3
+             (base, 260, 0, 0),           # 65 vectors: class 2
+             (base + 1, 2048, 4, 0),      # u8, head 15, body 2033 B -> 127 vectors + tail: 2
+             (base, 1024, 1, 0)]          # 2 KiB = 128 vectors: class 2
     img, info, _ = pack(descs, 0)
     _, items, _ = parse(img, info)
     n_block = info.n_items - info.n_small
-    n_full = info.n_small - info.n_half
-    full_rows = sorted(int(x["row"]) for x in items[n_block:n_block + n_full])
-    half_rows = sorted(int(x["row"]) for x in items[n_block + n_full:])
-    assert half_rows == [0, 1, 3, 4, 6]
-    assert full_rows == [2, 5, 7, 9]
+    rows = [sorted(int(items[i]["row"]) for i in range(n_block, info.n_items) if class_of(info, i) == c)
+            for c in range(4)]
+    assert rows == [[2, 5, 7, 9], [0, 1, 3, 4], [12, 13, 14], [6, 10, 11]]
     check_plan(descs, 0)
 
 
@@ -166,16 +181,17 @@ def test_wave_items_are_grouped_by_type():
     # each class of wave items is stored grouped by element type (stable within a type)
     base = 0x7F0000000000
     dts = [0, 1, 2, 1, 0, 2, 2, 1, 0, 0]
-    sizes = [100, 3000, 3000, 100, 1500, 100, 3000, 100, 1500, 100]   # half / full classes
+    sizes = [100, 3000, 3000, 100, 1500, 100, 3000, 100, 1500, 100]
     descs = [(base + (1 << 16) * k, n, dt, 0) for k, (dt, n) in enumerate(zip(dts, sizes))]
     img, info, _ = pack(descs, 0)
     _, items, _ = parse(img, info)
-    n_block = info.n_items - info.n_small
-    n_full = info.n_small - info.n_half
-    for lo, hi in ((n_block, n_block + n_full), (n_block + n_full, info.n_items)):
+    lo = info.n_items - info.n_small
+    for c in range(4):
+        hi = lo + info.n_wave[c]
         got = [(int(x["df"]) & 0xFF, int(x["row"])) for x in items[lo:hi]]
         assert got == sorted(got)
-    assert n_full == 5 and info.n_half == 5
+        lo = hi
+    assert list(info.n_wave) == [5, 0, 0, 5]
     check_plan(descs, 0)
 
 
