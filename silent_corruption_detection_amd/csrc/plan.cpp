@@ -1,5 +1,5 @@
 // plan.cpp -- host side of the scan plan: splitting a tensor list into
-// self-contained work items (workgroup items, then wave items), the
+// self-contained work items (workgroup items, then wave items by class), the
 // split-tensor table and partial-row slots, and the one host-to-device copy.
 #include <algorithm>
 #include <cstring>
@@ -17,8 +17,6 @@ struct Layout {
   uint64_t item_bytes = 0;
   PlanOffsets off{};
 };
-
-uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
 // Items of one tensor: [0, min(n, h + IE)), then IE elements at a time, where
 // h is the misaligned head and IE = item_bytes / es.  Calls f(start, len).

@@ -32,7 +32,11 @@
 //     form); a tensor scanned by one item stores its row, each item of a
 //     split tensor stores a partial row in its own slot, and one wave per
 //     split tensor combines its slots (+, +, ^, +: order independent, so the
-//     result is bit-exact, and no atomics share an address).
+//     result is bit-exact; no atomics).
+//   * Small tensors (aligned body <= 8 KiB) are wave items instead: a group
+//     of 64, 32, 16 or 8 lanes (the narrowest whose 8 vectors per lane hold
+//     the body) scans one whole with all its loads in flight at once, so a
+//     wave works on 1 to 8 of these latency-bound tensors together.
 #include <algorithm>
 
 #include "fingerprint_device.h"

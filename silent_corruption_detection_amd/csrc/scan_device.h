@@ -1,8 +1,8 @@
 // scan_device.h -- device building blocks shared by the scan-family kernels
 // (fingerprint, NaN/Inf count, squared norm): raw non-temporal buffer loads,
 // the exact per-type NaN/Inf rules and their fast pre-checks, element-type
-// dispatch, the head / aligned body / tail split of a work item, and the
-// wave index of wave items.
+// dispatch, the pipelined body stream of workgroup items, the head / aligned
+// body / tail split of a work item, and the lane groups of wave items.
 #pragma once
 
 #include <type_traits>
