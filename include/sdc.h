@@ -150,7 +150,9 @@ typedef struct {
 
 /* Device bytes needed for the plan of h_tensors[0..n).  item_bytes is the work
  * item size in bytes (a multiple of 16, at most 4 MiB); 0 selects it
- * automatically from the total size.  Host-only: no HIP call. */
+ * automatically: the largest power of two from 1 MiB down to 64 KiB that
+ * still splits the list into at least 49152 items (else 64 KiB).  The rows do
+ * not depend on it.  Host-only: no HIP call. */
 int32_t sdc_plan_bytes(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
                        uint64_t* h_bytes);
 

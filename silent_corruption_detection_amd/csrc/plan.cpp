@@ -71,7 +71,24 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
     elems += t[k].numel;
     bytes += t[k].numel * es;
   }
-  if (item_bytes == 0) item_bytes = auto_item_bytes(bytes);
+  if (item_bytes == 0) {
+    // items per candidate size kAutoMax >> c, counted in one pass
+    constexpr int kCand = 5;  // 1 MiB .. 64 KiB
+    static_assert((kAutoMax >> (kCand - 1)) == kAutoMin, "candidate sizes");
+    uint64_t cnt[kCand] = {0, 0, 0, 0, 0};
+    for (uint64_t k = 0; k < n; ++k) {
+      if (!has_data(t[k])) continue;
+      const uint64_t ptr = reinterpret_cast<uintptr_t>(t[k].ptr);
+      const uint32_t es = element_size(t[k].dtype);
+      for (int c = 0; c < kCand; ++c) cnt[c] += items_of(ptr, t[k].numel, es, kAutoMax >> c);
+    }
+    item_bytes = kAutoMin;
+    for (int c = 0; c < kCand; ++c)
+      if (cnt[c] >= kAutoMinItems) {
+        item_bytes = kAutoMax >> c;
+        break;
+      }
+  }
   uint64_t items = 0, small = 0, split = 0, slots = 0;
   uint64_t nw[kWaveClasses] = {0, 0, 0, 0};
   for (uint64_t k = 0; k < n; ++k) {
