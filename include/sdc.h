@@ -13,21 +13,26 @@
  *                                                 of the replicas' tables.
  *   [AEGIS] review page of "Safeguarding LLM Training at Scale: Online SDC
  *          Detection and Insights from 35 Million GPU Hours", section "core
- *          method" (核心方法) item 4 -- the xorsum fingerprint.
+ *          method" (核心方法) item 4 -- the xorsum fingerprint, and the
+ *          bitwise comparison of a result with its deterministic
+ *          recomputation.
  *
  * Conventions shared by every entry point
  *   - Every function returns an int32_t status (SDC_OK or a negative SDC_ERR_*).
  *     No C++ exception or abort crosses the ABI.
  *   - "d_" arguments are device pointers (HIP device memory of the current
  *     device), "h_" arguments are host pointers.  The caller owns and allocates
- *     all memory; the library allocates no device memory and keeps no state
- *     between calls other than a thread-local copy of the last HIP error.
+ *     all device memory; the library allocates none.  Between calls it keeps
+ *     only per-host-thread state: the last HIP error and a small host staging
+ *     buffer of the compare calls' single device-to-host copy.
  *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
  *     Functions documented as asynchronous only enqueue work on that stream;
  *     their device outputs are valid once the stream reaches that point.
- *   - All arithmetic is on unsigned 64-bit integers modulo 2^64; floating
- *     point data are read as raw bit patterns and never converted, so every
- *     result is exact and independent of launch shape and scheduling.
+ *   - The fingerprints are arithmetic on unsigned 64-bit integers modulo 2^64
+ *     over raw bit patterns (floating-point data are never converted), so
+ *     every row is exact and independent of launch shape and scheduling.  The
+ *     one floating-point result, sdc_sqnorm's squared norms, is summed in an
+ *     order fixed by the plan.
  *   - Functions are thread-safe.  Two scans that write the same output rows
  *     must not run concurrently.
  */
@@ -178,16 +183,16 @@ int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_by
  * start u64, len u32, row u32, slot u32, dtype | 0x100 if whole-tensor u32},
  * workgroup items first, then the n_small wave items (the n_wave[0..3] items
  * of each class in turn, each class ordered by element type); then n_split
- * 16-byte
- * entries {row, first slot, slot count, 0} (uint32 each). */
+ * 16-byte entries {row, first slot, slot count, 0} (uint32 each). */
 int32_t sdc_plan_pack_host(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
                            void* h_plan, uint64_t plan_bytes, sdc_plan_info* h_info);
 
 /* [BLOG] "Compare by fingerprint", [AEGIS] xorsum: writes d_out[k] = row of
  * tensor k for k < n_tensors (d_out: n_tensors * 32 bytes of device memory;
  * every row is written, previous contents do not matter).
- * ASYNCHRONOUS on stream: one scan launch, then one merge launch for the rows
- * of split (and missing/empty) tensors.  Errors: SDC_ERR_INVALID,
+ * ASYNCHRONOUS on stream: one launch for the wave items, one for the
+ * workgroup items, then one merge launch for the rows of split (and
+ * missing/empty) tensors.  Errors: SDC_ERR_INVALID,
  * SDC_ERR_PLAN, SDC_ERR_HIP. */
 int32_t sdc_fingerprint_plan(const void* d_plan, const sdc_plan_info* h_info, sdc_row* d_out,
                              sdc_stream_t stream);
