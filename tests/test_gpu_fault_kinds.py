@@ -10,6 +10,11 @@ of a small GPT-style parameter list, and then
     what the weighted sum is for);
   - the diff against a clean replica names exactly the faulted tensor, and a
     single bit flip is localised to its element and bit.
+And the worked example of section "Step 1" (one weight on three replicas,
+fixture tests/golden/worked_example.json) computed on the GPU: the update
+lands on the same bits everywhere; a wrong local gradient changes every copy
+alike (the majority cannot see it, and being finite the NaN/Inf check passes
+it); a weight corrupted on one replica after the step is named.
 """
 import json
 import os
@@ -85,9 +90,55 @@ def test_page_fault_kinds(case):
     assert only_sum["diverged"] == case["plain_sum_changes"]
     only_w = sdc.sdc_majority_compare(out, 3, T, col_mask=sdc.COL_WSUM)
     assert only_w["diverged"] == case["weighted_sum_changes"]
-    d = sdc.sdc_fingerprint_diff(out[:T].contiguous(), out[bad_r * T:(bad_r + 1) * T].contiguous())
+    faulted = out[bad_r * T:(bad_r + 1) * T].contiguous()
+    d = sdc.sdc_fingerprint_diff(out[:T].contiguous(), faulted)
     assert d["n_diff"] == 1 and d["indices"] == [bad_k]
     if flip is not None:
         assert d["hints"][0][:2] == flip
     else:
         assert d["hints"][0][1] == -1   # not a single bit flip
+
+
+def test_worked_example_on_the_gpu():
+    # AWS blog post, "Step 1: Detect with three checks in your training loop":
+    # one weight on three replicas (fixture tests/golden/worked_example.json)
+    g = json.load(open(os.path.join(HERE, "golden", "worked_example.json")))
+    R, lr = g["replicas"], g["learning_rate"]
+
+    def dp_step(grads):
+        # the all-reduce averages once, in rank order; every replica applies it
+        acc = torch.zeros(1, dtype=torch.float32, device=DEV)
+        for x in grads:
+            acc = acc + torch.tensor([x], dtype=torch.float32, device=DEV)
+        avg = acc / R
+        return [torch.tensor([w], dtype=torch.float32, device=DEV) - lr * avg
+                for w in g["weight_at_start"]]
+
+    def scan(ws):
+        plan = sdc.sdc_plan_build(ws)
+        out = sdc.sdc_fingerprint_plan(plan)
+        torch.cuda.synchronize()
+        return out
+
+    w1 = dp_step(g["local_gradient"])
+    bits = [int(t.view(torch.int32).item()) & 0xFFFFFFFF for t in w1]
+    assert bits == [int(np.array([v], dtype=np.float32).view(np.uint32)[0])
+                    for v in g["weight_after_step"]]
+    clean = scan(w1)
+    assert_rows_equal(sdc.rows_numpy(clean), oracle_rows(w1))
+    assert not sdc.sdc_majority_compare(clean, R, 1)["diverged"]
+    # a wrong local gradient reaches every replica: the copies still agree
+    bad = list(g["local_gradient"])
+    bad[g["faulty_local_gradient"]["replica"]] = g["faulty_local_gradient"]["value"]
+    w_bad = dp_step(bad)
+    t_bad = scan(w_bad)
+    assert not sdc.sdc_majority_compare(t_bad, R, 1)["diverged"]
+    assert sdc.sdc_fingerprint_diff(clean, t_bad)["n_diff"] == R   # but every copy changed
+    # the wrong gradient is finite: the NaN/Inf check passes it
+    grads = [torch.tensor([x], dtype=torch.float32, device=DEV) for x in bad]
+    _, _, flag = sdc.sdc_sqnorm(sdc.sdc_plan_build(grads))
+    assert int(flag.item()) == 0
+    # a weight corrupted on one replica after the step: that replica is named
+    W.flip_bit(w1[2], 0, 22)
+    res = sdc.sdc_majority_compare(scan(w1), R, 1)
+    assert res["diverged"] and res["suspects"] == [2]
