@@ -12,7 +12,7 @@ namespace sdc {
 namespace {
 
 // ---- NaN/Inf count only ----------------------------------------------------------
-template <class Ty>
+template <class Ty, int U>
 __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
   constexpr uint32_t es = Ty::ES;
   const uint32_t t = threadIdx.x;
@@ -26,7 +26,7 @@ __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
     if (sp.nvec) {
       const unsigned char* body = sp.base + (uint64_t)sp.h * es;
       Chk<Ty::CHK> chk(rule);
-      stream_body<kCheckU, true>(body, sp.nvec, [&](u32x4 v) { chk.add(v); });
+      stream_body<U, true>(body, sp.nvec, [&](u32x4 v) { chk.add(v); });
       if (chk.flagged()) {
         for (uint32_t vi = t; vi < sp.nvec; vi += kBlock) {
           __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
@@ -52,6 +52,7 @@ struct Unsigned {
   typedef TypeTag<Ty::ES, false, Ty::CHK> type;
 };
 
+template <int U>
 __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __restrict__ items,
                                                            sdc_row* __restrict__ partials,
                                                            uint64_t* __restrict__ counts,
@@ -59,7 +60,7 @@ __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __res
   const PlanItem it = items[blockIdx.x];
   uint32_t c = 0;
   dispatch_type(it.dtype_flags & ~kItemSigned,
-                [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type>(it); });
+                [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type, U>(it); });
   if (threadIdx.x != 0) return;
   if (counts) {
     if (it.dtype_flags & kItemWhole) counts[it.row] = c;
@@ -155,8 +156,12 @@ extern "C" int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info
     if ((st = launch_status())) return st;
   }
   if (n_block) {
-    hipLaunchKernelGGL(nonfinite_kernel, dim3((uint32_t)n_block), dim3(kBlock), 0, s, v.items,
-                       v.partials, d_counts, d_total);
+    if (h_info->total_bytes / h_info->n_items >= kCheckDeepItemBytes)
+      hipLaunchKernelGGL(nonfinite_kernel<kCheckDeepU>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
+                         v.items, v.partials, d_counts, d_total);
+    else
+      hipLaunchKernelGGL(nonfinite_kernel<kCheckU>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
+                         v.items, v.partials, d_counts, d_total);
     if ((st = launch_status())) return st;
   }
   if (d_counts && h_info->n_split) {
