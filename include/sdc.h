@@ -211,7 +211,7 @@ int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info, uint64_t*
  * from each floating-point type (raw integer types contribute 0) and summed
  * in double in an order fixed by the plan, so results are bit-reproducible
  * for a given plan (a different item size may change the last bits).
- * ASYNCHRONOUS.  Uses the plan's scratch rows, like a scan.  Errors as
+ * ASYNCHRONOUS.  Uses the plan's scratch area, like a scan.  Errors as
  * sdc_fingerprint_plan. */
 int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, double* d_sq,
                    double* d_total, uint32_t* d_flag, sdc_stream_t stream);

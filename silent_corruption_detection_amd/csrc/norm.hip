@@ -204,12 +204,28 @@ __global__ void __launch_bounds__(kBlock) merge_sq_kernel(const PlanSplit* __res
 
 // Total over all tensors in a fixed order, and the decision: the squared sum
 // rounded to fp32 is not finite.
-__global__ void __launch_bounds__(kBlock) sq_total_kernel(const double* __restrict__ sq, uint64_t n,
+// Sum of src[0..n) in a fixed order: thread t adds entries t, t + 256, ...,
+// then the fixed workgroup tree.
+__device__ __forceinline__ double ordered_sum(const double* __restrict__ src, uint64_t n) {
+  double acc = 0.0;
+  for (uint64_t k = threadIdx.x; k < n; k += kBlock) acc += src[k];
+  return block_sum_d(acc);
+}
+
+// Chunk c of the tensors' squared sums (kSqChunk tensors) -> chunks[c].
+__global__ void __launch_bounds__(kBlock) sq_chunk_kernel(const double* __restrict__ sq, uint64_t n,
+                                                          double* __restrict__ chunks) {
+  const uint64_t first = (uint64_t)blockIdx.x * kSqChunk;
+  const double acc = ordered_sum(sq + first, min(n - first, kSqChunk));
+  if (threadIdx.x == 0) chunks[blockIdx.x] = acc;
+}
+
+// The total from the tensors' sums (one chunk) or from the chunk sums, and
+// the decision: the squared sum rounded to fp32 is not finite.
+__global__ void __launch_bounds__(kBlock) sq_total_kernel(const double* __restrict__ src, uint64_t n,
                                                           double* __restrict__ total,
                                                           uint32_t* __restrict__ flag) {
-  double acc = 0.0;
-  for (uint64_t k = threadIdx.x; k < n; k += kBlock) acc += sq[k];
-  acc = block_sum_d(acc);
+  const double acc = ordered_sum(src, n);
   if (threadIdx.x == 0) {
     *total = acc;
     if (flag) *flag = !__builtin_isfinite((float)acc);
@@ -250,7 +266,18 @@ extern "C" int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, d
                        dim3(kBlock), 0, s, v.split, (uint32_t)h_info->n_split, v.partials, d_sq);
     if ((st = launch_status())) return st;
   }
-  hipLaunchKernelGGL(sq_total_kernel, dim3(1), dim3(kBlock), 0, s, d_sq, h_info->n_tensors, d_total,
-                     d_flag);
+  // The total in a fixed order: over the tensors directly when they fit one
+  // chunk, else over the chunk sums (the order depends on the plan only).
+  const uint64_t n_chunks = (h_info->n_tensors + kSqChunk - 1) / kSqChunk;
+  if (n_chunks > 1) {
+    hipLaunchKernelGGL(sq_chunk_kernel, dim3((uint32_t)n_chunks), dim3(kBlock), 0, s, d_sq,
+                       h_info->n_tensors, v.chunks);
+    if ((st = launch_status())) return st;
+    hipLaunchKernelGGL(sq_total_kernel, dim3(1), dim3(kBlock), 0, s, v.chunks, n_chunks, d_total,
+                       d_flag);
+  } else {
+    hipLaunchKernelGGL(sq_total_kernel, dim3(1), dim3(kBlock), 0, s, d_sq, h_info->n_tensors,
+                       d_total, d_flag);
+  }
   return launch_status();
 }

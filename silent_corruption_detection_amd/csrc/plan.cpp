@@ -119,7 +119,7 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
   L->total_elems = elems;
   L->total_bytes = bytes;
   L->item_bytes = item_bytes;
-  L->off = plan_offsets(items, split, slots);
+  L->off = plan_offsets(items, split, slots, n);
   return SDC_OK;
 }
 

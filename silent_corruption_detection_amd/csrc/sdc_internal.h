@@ -69,7 +69,8 @@ constexpr uint32_t kItemDtypeMask = 0xFFu;
 //   [PlanSplit  x n_split]   tensors not covered by exactly one item
 //   (pad to 256)
 //   [sdc_row    x n_slots]   partial rows of the items of split tensors
-// The partial rows are scratch written by every scan with this plan.
+//   [double     x ceil(n_tensors / kSqChunk)]   chunk sums of the squared norm
+// The partial rows and chunk sums are scratch written by the scans.
 struct PlanHeader {
   uint64_t magic;
   uint64_t n_tensors;
@@ -104,16 +105,21 @@ struct PlanSplit {
 };
 static_assert(sizeof(PlanSplit) == 16, "plan split layout");
 
+// Tensors per partial sum of the ordered squared-norm total.
+constexpr uint64_t kSqChunk = 4096;
+
 struct PlanOffsets {
-  uint64_t items, split, partials, end;
+  uint64_t items, split, partials, chunks, end;
 };
 
-inline PlanOffsets plan_offsets(uint64_t n_items, uint64_t n_split, uint64_t n_slots) {
+inline PlanOffsets plan_offsets(uint64_t n_items, uint64_t n_split, uint64_t n_slots,
+                                uint64_t n_tensors) {
   PlanOffsets o;
   o.items = sizeof(PlanHeader);
   o.split = o.items + n_items * sizeof(PlanItem);
   o.partials = (o.split + n_split * sizeof(PlanSplit) + 255) / 256 * 256;
-  o.end = o.partials + n_slots * sizeof(sdc_row);
+  o.chunks = o.partials + n_slots * sizeof(sdc_row);
+  o.end = o.chunks + (n_tensors + kSqChunk - 1) / kSqChunk * sizeof(double);
   return o;
 }
 
@@ -151,21 +157,23 @@ inline bool info_ok(const sdc_plan_info* h) {
   uint64_t w = 0;
   for (uint32_t c = 0; c < kWaveClasses; ++c) w += h->n_wave[c];
   if (w != h->n_small) return false;
-  return h->plan_bytes >= plan_offsets(h->n_items, h->n_split, h->n_slots).end;
+  return h->plan_bytes >= plan_offsets(h->n_items, h->n_split, h->n_slots, h->n_tensors).end;
 }
 
 struct PlanView {
   const PlanItem* items;
   const PlanSplit* split;
   sdc_row* partials;
+  double* chunks;
 };
 
 inline PlanView view_of(const void* d_plan, const sdc_plan_info* h) {
   unsigned char* base = reinterpret_cast<unsigned char*>(const_cast<void*>(d_plan));
-  const PlanOffsets o = plan_offsets(h->n_items, h->n_split, h->n_slots);
+  const PlanOffsets o = plan_offsets(h->n_items, h->n_split, h->n_slots, h->n_tensors);
   return PlanView{reinterpret_cast<const PlanItem*>(base + o.items),
                   reinterpret_cast<const PlanSplit*>(base + o.split),
-                  reinterpret_cast<sdc_row*>(base + o.partials)};
+                  reinterpret_cast<sdc_row*>(base + o.partials),
+                  reinterpret_cast<double*>(base + o.chunks)};
 }
 
 

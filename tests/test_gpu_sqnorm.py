@@ -186,3 +186,20 @@ def test_rejects_bad_arguments():
     sq = torch.empty(1, dtype=torch.float64, device=DEV)
     assert L.sdc_sqnorm(plan.buf.data_ptr(), ctypes.byref(bad), sq.data_ptr(), total.data_ptr(),
                         None, None) == -6
+
+
+def test_total_over_many_tensors():
+    # more tensors than one chunk of the ordered total (4096): chunk sums, then
+    # their sum; the total is within the bound of the oracle's and repeatable
+    g = gen(31)
+    sizes = torch.randint(1, 3000, (20_001,), generator=torch.Generator().manual_seed(5)).tolist()
+    big = torch.empty(sum(sizes), dtype=torch.float32, device=DEV).normal_(0, 1.0, generator=g)
+    tensors = list(torch.split(big, sizes))
+    say(f"case sqnorm many tensors n={len(tensors)}")
+    sq, total, flag = check(tensors)
+    assert flag == 0
+    plan = sdc.sdc_plan_build(tensors)
+    _, t1, _ = sdc.sdc_sqnorm(plan)
+    _, t2, _ = sdc.sdc_sqnorm(plan)
+    torch.cuda.synchronize()
+    assert float(t1.item()) == float(t2.item())
