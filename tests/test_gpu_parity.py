@@ -346,3 +346,24 @@ def test_tensor_with_more_than_2_32_elements(dtype, signed):
     assert_rows_equal(sdc.rows_numpy(r), ref)
     del raw, t
     torch.cuda.empty_cache()
+
+
+def test_non_contiguous_inputs_use_logical_order():
+    # the pages' fingerprint reads a tensor's contiguous (row-major) form; the
+    # one-shot and single-tensor scans copy a strided view first, a plan refuses it
+    g = gen(41)
+    a = torch.empty((300, 517), dtype=torch.float32, device=DEV).normal_(0, 1, generator=g)
+    b = torch.empty((64, 33, 7), dtype=torch.float32, device=DEV).normal_(0, 1,
+                                                                          generator=g).bfloat16()
+    views = [a.t(), a[:, ::3], b.permute(2, 0, 1), b[::2, 1:]]
+    assert not any(v.is_contiguous() for v in views)
+    ref = oracle_rows([v.contiguous() for v in views])
+    out = sdc.sdc_fingerprint(views)
+    torch.cuda.synchronize()
+    assert_rows_equal(sdc.rows_numpy(out), ref)
+    for k, v in enumerate(views):
+        r = sdc.sdc_fingerprint_tensor(v)
+        torch.cuda.synchronize()
+        assert_rows_equal(sdc.rows_numpy(r), ref[k:k + 1])
+    with pytest.raises(ValueError):
+        sdc.sdc_plan_build(views)
