@@ -25,6 +25,7 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
+ABI_VERSION = 2  # SDC_ABI_VERSION of include/sdc.h that the structs below mirror
 
 (F32, BF16, F16, F64, U8, FP8_E4M3, FP8_E5M2, FP8_E4M3FNUZ, FP8_E5M2FNUZ, U16, U32,
  U64) = range(12)
@@ -98,6 +99,9 @@ def _load():
     L.sdc_last_hip_error.restype = I32
     L.sdc_abi_version.argtypes = []
     L.sdc_abi_version.restype = U32
+    if L.sdc_abi_version() != ABI_VERSION:  # struct layouts below would not match
+        raise ImportError(f"{LIB_PATH} has ABI {L.sdc_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}; rebuild it with __graft_entry__.build()")
     return L
 
 
