@@ -61,6 +61,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def build_plan(sdc, torch, tensors):
+    """The plan (packing on the host + one upload), and its wall time in ms: a
+    one-time cost per tensor list, reported beside the scan, not inside it."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    plan = sdc.sdc_plan_build(tensors)
+    return plan, round((time.perf_counter() - t0) * 1000.0, 3)
+
+
 def time_steps(step, K, W, stream):
     import torch
     for _ in range(W):
@@ -80,7 +89,7 @@ def time_steps(step, K, W, stream):
 def bench_c5(args, torch, sdc, W_):
     log("bench: generating the Llama-70B bf16 list (141 GB) ...")
     w = W_.c5("cuda")
-    plan = sdc.sdc_plan_build(w.tensors)
+    plan, plan_ms = build_plan(sdc, torch, w.tensors)
     stream = torch.cuda.current_stream()
     stored = sdc.sdc_fingerprint_plan(plan).clone()  # the fingerprint table stored at checkpoint time
     out = torch.empty_like(stored)
@@ -101,13 +110,13 @@ def bench_c5(args, torch, sdc, W_):
     ms, kms = time_steps(step, args.steps, args.warmup, stream)
     if bad:
         raise RuntimeError(f"scan is not reproducible: {bad[:2]}")
-    return w, plan, out, ms, kms
+    return w, plan, out, ms, kms, plan_ms
 
 
 def bench_c2(args, torch, sdc, W_):
     log("bench: generating the GPT-style 0.96B fp32 list x 3 replicas ...")
     w = W_.c2("cuda")
-    plan = sdc.sdc_plan_build(w.tensors)
+    plan, plan_ms = build_plan(sdc, torch, w.tensors)
     stream = torch.cuda.current_stream()
     out = sdc.sdc_fingerprint_plan(plan)
     torch.cuda.synchronize()
@@ -128,7 +137,8 @@ def bench_c2(args, torch, sdc, W_):
                 elements=plan.total_elems, bytes=plan.total_bytes, item_bytes=plan.item_bytes,
                 ms_per_step=round(ms, 4), value=round(plan.total_bytes / ms / 1e6, 1),
                 unit="GB/s", kernel_ms=round(kms, 4),
-                kernel_frac_of_hbm_peak=round(plan.total_bytes / kms / 1e6 / HBM_PEAK_GBS, 4))
+                kernel_frac_of_hbm_peak=round(plan.total_bytes / kms / 1e6 / HBM_PEAK_GBS, 4),
+                plan_build_ms=plan_ms)
     del w, plan, out
     return info
 
@@ -138,7 +148,7 @@ def bench_other(args, torch, sdc, W_, name):
     small tensors): scan + the comparison each is for, and for c3 the
     NaN/Inf-count and squared-norm launches on their own."""
     w = W_.BUILDERS[name]("cuda")
-    plan = sdc.sdc_plan_build(w.tensors)
+    plan, plan_ms = build_plan(sdc, torch, w.tensors)
     stream = torch.cuda.current_stream()
     out = sdc.sdc_fingerprint_plan(plan)
     counts = torch.empty(max(plan.n_tensors, 1), dtype=torch.int64, device="cuda")
@@ -162,7 +172,8 @@ def bench_other(args, torch, sdc, W_, name):
                bytes=plan.total_bytes, item_bytes=plan.item_bytes, work_items=plan.n_items,
                ms_per_step=round(ms, 4), value=round(plan.total_bytes / ms / 1e6, 1), unit="GB/s",
                kernel_ms=round(kms, 4), kernel_gbs=round(plan.total_bytes / kms / 1e6, 1),
-               kernel_frac_of_hbm_peak=round(plan.total_bytes / kms / 1e6 / HBM_PEAK_GBS, 4))
+               kernel_frac_of_hbm_peak=round(plan.total_bytes / kms / 1e6 / HBM_PEAK_GBS, 4),
+               plan_build_ms=plan_ms)
     if name == "c3":
         def nf_step(ev):
             if ev is not None:
@@ -309,7 +320,7 @@ def main():
     if not args.no_secondary:
         secondary = bench_c2(args, torch, sdc, W_)
         torch.cuda.empty_cache()
-    w, plan, out, ms, kms = bench_c5(args, torch, sdc, W_)
+    w, plan, out, ms, kms, plan_ms = bench_c5(args, torch, sdc, W_)
     total_bytes = plan.total_bytes
     achieved = total_bytes / kms / 1e6  # GB/s
     traffic = traffic_from_profile("llama70b_bf16")
@@ -330,6 +341,7 @@ def main():
                      "traffic": traffic, "kernel": "fingerprint_kernel (+ merge_rows_kernel)",
                      "kernel_ms": round(kms, 4), "kernel_hash": kernel_hash()},
         "elements_per_s": round(plan.total_elems / ms * 1e3, 1),
+        "plan_build_ms": plan_ms,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "cpu_baseline": cpu,
         "secondary": secondary,

@@ -140,34 +140,54 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+# sdc_tensor as a numpy record: the descriptor table is filled column by
+# column (a per-tensor ctypes struct costs ~1 us, too slow for 10^5 tensors).
+_DESC = np.dtype([("ptr", "<u8"), ("numel", "<u8"), ("dtype", "<u4"), ("flags", "<u4")])
+assert _DESC.itemsize == ctypes.sizeof(_Tensor)
+
+
+class _DescTable:
+    """A host sdc_tensor array passed to the library as a pointer."""
+
+    def __init__(self, n):
+        self.array = np.zeros(max(n, 1), dtype=_DESC)
+        self._as_parameter_ = ctypes.c_void_p(self.array.ctypes.data)
+
+
 def _descriptors(tensors, require_contiguous, signed=False):
-    """Tensor list -> (ctypes array of sdc_tensor, device, kept tensors).
-    signed: widen 2-/4-byte patterns with sign extension (SDC_FLAG_SIGNED),
-    as the pages' own fingerprint function does."""
+    """Tensor list -> (sdc_tensor table, device, kept tensors).  None entries
+    are missing tensors (zero rows).  signed: widen 2-/4-byte patterns with
+    sign extension (SDC_FLAG_SIGNED), as the pages' own fingerprint function
+    does."""
     n = len(tensors)
-    flags = FLAG_SIGNED if signed else 0
-    arr = (_Tensor * max(n, 1))()
-    device, keep = None, []
-    for k, t in enumerate(tensors):
-        if t is None:
-            arr[k] = _Tensor(None, 0, F32, 0)
-            continue
-        if t.dtype not in _TORCH_DTYPE:
-            raise TypeError(f"tensor {k}: unsupported dtype {t.dtype}")
-        if not t.is_cuda:
-            raise ValueError(f"tensor {k} is not on a GPU")
-        if device is None:
-            device = t.device
-        elif t.device != device:
-            raise ValueError(f"tensor {k} is on {t.device}, expected {device}")
-        if not t.is_contiguous():
-            if require_contiguous:
-                raise ValueError(f"tensor {k} is not contiguous (a plan reads it in place)")
-            t = t.contiguous()
-        keep.append(t)
-        arr[k] = _Tensor(t.data_ptr() if t.numel() else None, t.numel(), _TORCH_DTYPE[t.dtype],
-                         flags)
-    return arr, device, keep
+    table = _DescTable(n)
+    idx = [k for k, t in enumerate(tensors) if t is not None]
+    ts = [tensors[k] for k in idx] if len(idx) != n else list(tensors)
+    if not ts:
+        return table, None, []
+    codes = [_TORCH_DTYPE.get(t.dtype) for t in ts]
+    if None in codes:
+        j = codes.index(None)
+        raise TypeError(f"tensor {idx[j]}: unsupported dtype {ts[j].dtype}")
+    devs = [t.get_device() for t in ts]
+    if min(devs) < 0:
+        raise ValueError(f"tensor {idx[devs.index(min(devs))]} is not on a GPU")
+    if max(devs) != min(devs):
+        j = next(j for j, d in enumerate(devs) if d != devs[0])
+        raise ValueError(f"tensor {idx[j]} is on cuda:{devs[j]}, expected cuda:{devs[0]}")
+    contig = [t.is_contiguous() for t in ts]
+    if not all(contig):
+        if require_contiguous:
+            j = contig.index(False)
+            raise ValueError(f"tensor {idx[j]} is not contiguous (a plan reads it in place)")
+        ts = [t if c else t.contiguous() for t, c in zip(ts, contig)]
+    numels = [t.numel() for t in ts]
+    a = table.array
+    a["ptr"][idx] = [t.data_ptr() if m else 0 for t, m in zip(ts, numels)]
+    a["numel"][idx] = numels
+    a["dtype"][idx] = codes
+    a["flags"][idx] = FLAG_SIGNED if signed else 0
+    return table, torch.device("cuda", devs[0]), ts
 
 
 def sdc_plan_bytes(tensors, item_bytes=0):
