@@ -9,6 +9,7 @@ Function names are those of the C ABI.
 """
 import ctypes
 import os
+import threading
 
 import numpy as np
 import torch
@@ -132,6 +133,23 @@ def sdc_last_hip_error():
 
 def sdc_abi_version():
     return _lib.sdc_abi_version()
+
+
+_tls = threading.local()
+
+
+def _sync_ws(nbytes, device):
+    """Workspace of the synchronous calls (compare, diff, ring audit): they
+    return only after their stream has finished with it, so one buffer per
+    host thread and device is reused from call to call."""
+    cache = getattr(_tls, "ws", None)
+    if cache is None:
+        cache = _tls.ws = {}
+    key = torch.device(device)
+    ws = cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = cache[key] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=key)
+    return ws
 
 
 def _stream_handle(stream, device):
@@ -353,7 +371,7 @@ def sdc_majority_compare(table, R, T=None, col_mask=COL_ALL, tensor_status=None,
     if table.dtype != torch.int64 or not table.is_contiguous() or table.numel() < R * T * 4:
         raise ValueError("table must be a contiguous int64 [R*T, 4] device tensor")
     dev = table.device
-    ws = torch.empty(max(sdc_majority_ws_bytes(R, T), 1), dtype=torch.uint8, device=dev)
+    ws = _sync_ws(sdc_majority_ws_bytes(R, T), dev)
     res = _Majority()
     sus = (ctypes.c_uint8 * max(R, 1))()
     st_ptr = None
@@ -389,7 +407,7 @@ def sdc_fingerprint_diff(a, b, col_mask=COL_ALL, idx_cap=None, hints=True, strea
     T = a.shape[0]
     cap = T if idx_cap is None else idx_cap
     dev = a.device
-    ws = torch.empty(max(sdc_diff_ws_bytes(T, cap), 1), dtype=torch.uint8, device=dev)
+    ws = _sync_ws(sdc_diff_ws_bytes(T, cap), dev)
     n = ctypes.c_uint64(0)
     idx = (ctypes.c_uint64 * max(cap, 1))()
     hs = (_FlipHint * max(cap, 1))() if hints else None
@@ -421,7 +439,7 @@ def sdc_ring_compare(table, n, offset, stream=None):
     if table.dtype != torch.int64 or not table.is_contiguous() or table.numel() % (2 * n):
         raise ValueError("table must be a contiguous int64 [n, 2, width] device tensor")
     width = table.numel() // (2 * n)
-    ws = torch.empty(sdc_ring_ws_bytes(n), dtype=torch.uint8, device=table.device)
+    ws = _sync_ws(sdc_ring_ws_bytes(n), table.device)
     flags = (ctypes.c_uint8 * n)()
     _check(_lib.sdc_ring_compare(ctypes.c_void_p(table.data_ptr()), n, width, offset,
                                  ctypes.c_void_p(ws.data_ptr()), ws.numel(), flags,
@@ -446,7 +464,7 @@ def sdc_confirm_verdict(third, self_, orig, peer, stream=None):
     for v in vs:
         if v.dtype != torch.int64 or not v.is_contiguous() or v.numel() != width:
             raise ValueError("the four results must be contiguous int64 tensors of one length")
-    ws = torch.empty(sdc_ring_ws_bytes(1), dtype=torch.uint8, device=third.device)
+    ws = _sync_ws(sdc_ring_ws_bytes(1), third.device)
     out = ctypes.c_int32(0)
     _check(_lib.sdc_confirm_verdict(*[ctypes.c_void_p(v.data_ptr()) for v in vs], width,
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.byref(out),
