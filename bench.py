@@ -286,9 +286,9 @@ def main():
                          "reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the scan runs on each GPU's own replica and would need only a small "
-              "all-gather of fingerprint tables across GPUs, which is not part of this build)",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(each GPU would scan its own replica and exchange only a small all-gather of "
+              "fingerprint tables, which this library does not implement)",
               file=sys.stderr)
         sys.exit(2)
 
