@@ -10,9 +10,10 @@ end of a recomputed segment covers the whole segment with one comparison.
 
 `RecomputeAudit.wrap(fn, k)` returns the function to hand to
 `torch.utils.checkpoint.checkpoint` for segment k.  The first call of segment
-k in a step (the forward pass) stores the row of its output; the second (the
-recomputation in backward) scans the recomputed output, compares it with the
-stored row on the device and counts a difference.  Every scan is
+k in a step (the forward pass) stores the rows of its outputs (a tensor, or a
+tuple of up to `outputs` tensors); the second (the recomputation in
+backward) scans the recomputed outputs, compares them with the stored rows
+on the device and counts differences.  Every scan is
 `sdc_fingerprint_tensor`: asynchronous on the current stream, no plan upload,
 no host synchronisation.  `result()` is the step's one synchronisation.
 
@@ -30,13 +31,19 @@ from . import (COL_ALL, rows_numpy, sdc_fingerprint_diff, sdc_fingerprint_tensor
 
 
 class RecomputeAudit:
-    def __init__(self, n_segments, device="cuda", col_mask=COL_ALL):
-        if n_segments < 1:
-            raise ValueError("need at least one segment")
+    """Fingerprints of each checkpointed segment's outputs (up to `outputs`
+    tensors per segment), stored at forward time and compared on the device
+    when backward recomputes them."""
+
+    def __init__(self, n_segments, device="cuda", col_mask=COL_ALL, outputs=1):
+        if n_segments < 1 or outputs < 1:
+            raise ValueError("need at least one segment and one output per segment")
         self.n = n_segments
+        self.outputs = outputs
         self.col_mask = col_mask
         dev = torch.device(device)
-        self.original = torch.zeros((n_segments, 4), dtype=torch.int64, device=dev)
+        # row k * outputs + j: output j of segment k
+        self.original = torch.zeros((n_segments * outputs, 4), dtype=torch.int64, device=dev)
         self.recomputed = torch.zeros_like(self.original)
         self.mismatch = torch.zeros(n_segments, dtype=torch.int32, device=dev)
         self.calls = [0] * n_segments
@@ -57,7 +64,8 @@ class RecomputeAudit:
         self.calls = [0] * self.n
 
     def wrap(self, fn, k):
-        """fn(*args) -> tensor, as segment k of a checkpointed model."""
+        """fn(*args) -> a tensor, or a tuple/list of tensors (None entries are
+        skipped), as segment k of a checkpointed model."""
         if not 0 <= k < self.n:
             raise IndexError(f"segment {k} out of range 0..{self.n - 1}")
 
@@ -68,34 +76,45 @@ class RecomputeAudit:
         return run
 
     def record(self, k, out):
-        if not isinstance(out, torch.Tensor):
-            raise TypeError(f"segment {k} must return one tensor, got {type(out).__name__}")
+        outs = (out,) if isinstance(out, torch.Tensor) else out
+        if not isinstance(outs, (tuple, list)) or len(outs) > self.outputs or not all(
+                o is None or isinstance(o, torch.Tensor) for o in outs):
+            raise TypeError(f"segment {k} must return a tensor or up to {self.outputs} tensors")
         c = self.calls[k]
-        t = out.detach()
-        if c == 0:
-            sdc_fingerprint_tensor(t, out=self.original[k:k + 1], ws=self._workspace(t))
-        elif c == 1:
-            sdc_fingerprint_tensor(t, out=self.recomputed[k:k + 1], ref=self.original[k:k + 1],
-                                   mismatch=self.mismatch[k:k + 1], col_mask=self.col_mask,
-                                   ws=self._workspace(t))
-        else:
+        if c > 1:
             raise RuntimeError(f"segment {k} ran {c + 1} times in one step (call begin_step())")
+        for j, o in enumerate(outs):
+            if o is None:
+                continue
+            t = o.detach()
+            r = k * self.outputs + j
+            if c == 0:
+                sdc_fingerprint_tensor(t, out=self.original[r:r + 1], ws=self._workspace(t))
+            else:
+                sdc_fingerprint_tensor(t, out=self.recomputed[r:r + 1], ref=self.original[r:r + 1],
+                                       mismatch=self.mismatch[k:k + 1], col_mask=self.col_mask,
+                                       ws=self._workspace(t))
         self.calls[k] = c + 1
 
     def result(self):
         """After backward (synchronises): segments whose recomputation differed
-        from the original, segments not recomputed, and for each mismatch the
-        single-bit-flip localisation of the two rows when there is one."""
+        from the original, segments not recomputed or not run, for each
+        mismatched segment the outputs that differ, and the single-bit-flip
+        localisation of its first differing output when there is one."""
         mism = self.mismatch.cpu().tolist()
         bad = [k for k in range(self.n) if mism[k]]
-        hints = {}
+        hints, outs = {}, {}
         if bad:
             d = sdc_fingerprint_diff(self.original, self.recomputed, col_mask=self.col_mask)
-            hints = {k: h for k, h in zip(d["indices"], d["hints"]) if k in bad}
+            for r, h in zip(d["indices"], d["hints"]):
+                k, j = divmod(r, self.outputs)
+                if k in bad:
+                    outs.setdefault(k, []).append(j)
+                    hints.setdefault(k, h)
         return {"mismatched": bad,
                 "not_recomputed": [k for k in range(self.n) if self.calls[k] == 1],
                 "not_run": [k for k in range(self.n) if self.calls[k] == 0],
-                "hints": hints}
+                "outputs": outs, "hints": hints}
 
     def rows(self):
         """Host uint64 copies of the original and recomputed rows."""

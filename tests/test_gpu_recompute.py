@@ -230,3 +230,34 @@ def test_flip_in_a_recomputed_output_is_localised():
     assert res["mismatched"] == [1]
     i, b, _ = res["hints"][1]
     assert (i, b) == (idx, bit)
+
+
+def test_segments_with_several_outputs():
+    # a segment returning (hidden, residual): each output has its own row; a
+    # flip in the recomputed residual is reported for that segment and output
+    n, d = 3, 256
+    model = make_model(d, n, torch.float32, seed=8)
+    x = torch.randn(512, d, device=DEV, generator=gen(9)).requires_grad_(True)
+    audit = RecomputeAudit(n, outputs=2)
+    calls = [0] * n
+
+    def seg(k):
+        def f(h, r):
+            out = model[k](h)
+            res = r + out
+            if k == 1 and calls[k] == 1:   # the recomputation of segment 1 goes wrong
+                W.flip_bit(res.data.reshape(-1), 777, 3)
+            calls[k] += 1
+            return out, res
+        return audit.wrap(f, k)
+
+    audit.begin_step()
+    h, r = x, torch.zeros_like(x)
+    for k in range(n):
+        h, r = cp.checkpoint(seg(k), h, r, use_reentrant=True)
+    (h.float().pow(2).mean() + r.float().pow(2).mean()).backward()
+    res = audit.result()
+    assert res["mismatched"] == [1] and res["outputs"] == {1: [1]}
+    assert res["hints"][1][:2] == (777, 3)
+    orig, rec = audit.rows()
+    assert np.array_equal(np.delete(orig, 3, axis=0), np.delete(rec, 3, axis=0))
