@@ -158,6 +158,11 @@ typedef BodyCfg<8, true> DeepBody;     // ~188 VGPRs: deeper pipeline, 2 workgro
 // Plans whose items average at least this many bytes use DeepBody (measured:
 // better for items of ~170 KiB and more, worse for lists of small tensors).
 constexpr uint64_t kDeepItemBytes = 96ull << 10;
+// NaN/Inf exact counts: bodies of at least this many vectors per lane per
+// round count a flagged round from its registers; shorter rounds (where a
+// check per round measurably slows lists of small tensors) keep one flag per
+// item and, when it is set, re-read the lane's vectors in a second pass.
+constexpr int kRoundCheckMinU = 8;
 // Body of one item: nvec aligned vectors at `body`.  Lane t handles vectors
 // 256*it + t, it = 0 .. T-1 with T = rounds*U (uniform over the workgroup);
 // vectors past the end are not loaded and count as zero vectors, which leave
@@ -170,21 +175,23 @@ __device__ __forceinline__ void scan_body(const unsigned char* body, uint32_t nv
   constexpr uint32_t E = kVecBytes / Ty::ES;    // elements per vector
   const uint32_t t = threadIdx.x;
   A_t acc(rule);
-  const uint32_t rounds = stream_body<U, Cfg::PIPE>(body, nvec, [&](u32x4 v) { acc.add(v); });
+  uint32_t nf = 0;
+  uint32_t rounds;
+  if constexpr (U >= kRoundCheckMinU) {
+    rounds = stream_body<U, Cfg::PIPE>(
+        body, nvec, [&](u32x4 v) { acc.add(v); },
+        [&](const u32x4 (&v)[U]) { count_flagged_round(acc.chk, v, nf); });
+  } else {
+    rounds = stream_body<U, Cfg::PIPE>(body, nvec, [&](u32x4 v) { acc.add(v); });
+    if (acc.chk.flagged())  // rare: a second, pipelined pass over this lane's vectors
+      stream_body<U, Cfg::PIPE>(body, nvec, [&](u32x4 v) { nf += acc.chk.exact(v); });
+  }
   const uint64_t T = (uint64_t)rounds * U;
   const uint64_t A = acc.sum();
   ln.s += A;
   ln.w += (uint64_t)(h + 1u + E * t) * A + (uint64_t)(kBlock * E) * (T * A - acc.q) + acc.csum();
   ln.x ^= acc.x;
-  if (acc.chk.flagged()) {
-    // Rare: some element may be NaN/Inf.  Recount this lane's vectors exactly.
-    uint32_t c = 0;
-    for (uint32_t vi = t; vi < nvec; vi += kBlock) {
-      __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
-      c += nf_vec<Ty::ES>(load16(rs, 0), rule);
-    }
-    ln.nf += c;
-  }
+  ln.nf += nf;
 }
 
 template <uint32_t ES, bool SIGNED>
@@ -311,7 +318,7 @@ __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane&
     ln.s += A;
     ln.w += (uint64_t)(sp.h + 1u + E * l) * A + (uint64_t)(LANES * E) * (T * A - acc.q) + acc.csum();
     ln.x ^= acc.x;
-    if (acc.chk.flagged()) {  // rare: reload this lane's vectors and count exactly
+    if (acc.chk.flagged()) {  // rare: reload this lane's (at most 8) vectors and count exactly
       uint32_t c = 0;
       for (uint32_t vi = l; vi < sp.nvec; vi += LANES)
         c += nf_vec<es>(load16_nt(body + (uint64_t)vi * kVecBytes), rule);

@@ -4,8 +4,8 @@
 //
 // Same items and traversal as the fingerprint scan, but only the fast
 // "may hold NaN/Inf" flag is computed per lane; a lane whose flag is set
-// recounts its own vectors with the type's exact rule.  Raw integer tensors
-// are never read.
+// after a round counts that round's vectors (still in registers) with the
+// type's exact rule.  Raw integer tensors are never read.
 #include "scan_device.h"
 
 namespace sdc {
@@ -26,13 +26,8 @@ __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
     if (sp.nvec) {
       const unsigned char* body = sp.base + (uint64_t)sp.h * es;
       Chk<Ty::CHK> chk(rule);
-      stream_body<U, true>(body, sp.nvec, [&](u32x4 v) { chk.add(v); });
-      if (chk.flagged()) {
-        for (uint32_t vi = t; vi < sp.nvec; vi += kBlock) {
-          __amdgpu_buffer_rsrc_t rs = make_rsrc(body + (uint64_t)vi * kVecBytes, kVecBytes);
-          c += nf_vec<es>(load16(rs, 0), rule);
-        }
-      }
+      stream_body<U, true>(body, sp.nvec, [&](u32x4 v) { chk.add(v); },
+                           [&](const u32x4 (&v)[U]) { count_flagged_round(chk, v, c); });
     }
   }
 #pragma unroll

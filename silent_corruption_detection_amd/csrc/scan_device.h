@@ -85,8 +85,8 @@ __device__ __forceinline__ uint32_t nf_vec(u32x4 v, const NfRule& r) {
 }
 
 // Fast "may contain NaN/Inf" flag, per element-type family.  Every NaN/Inf
-// sets it; a set flag triggers the exact recount, so false alarms only cost
-// time.
+// sets it; a set flag triggers an exact count of the vectors it covers (then
+// reset()), so false alarms only cost time.
 enum : int { kChkNone = 0, kChkHalf = 1, kChkF32 = 2, kChkF64 = 3, kChkFp8Top = 4, kChkFp8Eq = 5 };
 
 template <int CHK>
@@ -97,6 +97,8 @@ struct Chk<kChkNone> {  // raw integers: never NaN/Inf
   __device__ __forceinline__ explicit Chk(const NfRule&) {}
   __device__ __forceinline__ void add(u32x4) {}
   __device__ __forceinline__ bool flagged() const { return false; }
+  __device__ __forceinline__ void reset() {}
+  __device__ __forceinline__ uint32_t exact(u32x4) const { return 0u; }
 };
 
 // bf16 / fp16: fma(x, 0, acc) on the dword read as two fp16 halves stays +0
@@ -105,7 +107,9 @@ struct Chk<kChkNone> {  // raw integers: never NaN/Inf
 template <>
 struct Chk<kChkHalf> {
   h2 nf = {0, 0};
-  __device__ __forceinline__ explicit Chk(const NfRule&) {}
+  uint32_t m2, k2;  // the exponent mask in both halves; 0x8000 - mask in both halves
+  __device__ __forceinline__ explicit Chk(const NfRule& r)
+      : m2((uint32_t)r.mask * 0x10001u), k2((0x8000u - (uint32_t)r.mask) * 0x10001u) {}
   __device__ __forceinline__ void add(u32x4 v) {
     const h2 z = {0, 0};
     nf = __builtin_elementwise_fma(as_h2(v.x), z, nf);
@@ -114,6 +118,15 @@ struct Chk<kChkHalf> {
     nf = __builtin_elementwise_fma(as_h2(v.w), z, nf);
   }
   __device__ __forceinline__ bool flagged() const { return h2_bits(nf) != 0; }
+  __device__ __forceinline__ void reset() { nf = h2{0, 0}; }
+  // Exact count: per half, (x & m) + (0x8000 - m) reaches bit 15 exactly when
+  // every exponent bit is set, and never carries into the other half.
+  __device__ __forceinline__ uint32_t one(uint32_t d) const {
+    return (uint32_t)__builtin_popcount(((d & m2) + k2) & 0x80008000u);
+  }
+  __device__ __forceinline__ uint32_t exact(u32x4 v) const {
+    return one(v.x) + one(v.y) + one(v.z) + one(v.w);
+  }
 };
 
 template <>
@@ -127,6 +140,14 @@ struct Chk<kChkF32> {  // exact: fma(x, 0, acc) is NaN iff x is NaN/Inf
     nf = __builtin_fmaf(__uint_as_float(v.w), 0.0f, nf);
   }
   __device__ __forceinline__ bool flagged() const { return __float_as_uint(nf) != 0u; }
+  __device__ __forceinline__ void reset() { nf = 0.0f; }
+  // exponent bits 30..23 all ones: adding 1 at bit 23 carries into bit 31
+  __device__ __forceinline__ static uint32_t one(uint32_t d) {
+    return ((d & 0x7F800000u) + 0x00800000u) >> 31;
+  }
+  __device__ __forceinline__ uint32_t exact(u32x4 v) const {
+    return one(v.x) + one(v.y) + one(v.z) + one(v.w);
+  }
 };
 
 template <>
@@ -138,6 +159,12 @@ struct Chk<kChkF64> {  // exact, as for fp32
     nf = __builtin_fma(__longlong_as_double((long long)lohi(v.z, v.w)), 0.0, nf);
   }
   __device__ __forceinline__ bool flagged() const { return __double_as_longlong(nf) != 0; }
+  __device__ __forceinline__ void reset() { nf = 0.0; }
+  // exponent bits 62..52 = bits 30..20 of the high word
+  __device__ __forceinline__ static uint32_t one(uint32_t hi) {
+    return ((hi & 0x7FF00000u) + 0x00100000u) >> 31;
+  }
+  __device__ __forceinline__ uint32_t exact(u32x4 v) const { return one(v.y) + one(v.w); }
 };
 
 // fp8 whose NaN/Inf are "all ones under a mask m < 0x80" (E4M3: m = 0x7F,
@@ -148,13 +175,19 @@ struct Chk<kChkFp8Top> {
   uint32_t flag = 0, m4, k4;
   __device__ __forceinline__ explicit Chk(const NfRule& r)
       : m4((uint32_t)r.mask * 0x01010101u), k4((0x80u - (uint32_t)r.mask) * 0x01010101u) {}
+  __device__ __forceinline__ uint32_t bits(uint32_t d) const { return ((d & m4) + k4) & 0x80808080u; }
   __device__ __forceinline__ void add(u32x4 v) {
-    flag |= ((v.x & m4) + k4) & 0x80808080u;
-    flag |= ((v.y & m4) + k4) & 0x80808080u;
-    flag |= ((v.z & m4) + k4) & 0x80808080u;
-    flag |= ((v.w & m4) + k4) & 0x80808080u;
+    flag |= bits(v.x);
+    flag |= bits(v.y);
+    flag |= bits(v.z);
+    flag |= bits(v.w);
   }
   __device__ __forceinline__ bool flagged() const { return flag != 0; }
+  __device__ __forceinline__ void reset() { flag = 0; }
+  __device__ __forceinline__ uint32_t exact(u32x4 v) const {
+    return (uint32_t)(__builtin_popcount(bits(v.x)) + __builtin_popcount(bits(v.y)) +
+                      __builtin_popcount(bits(v.z)) + __builtin_popcount(bits(v.w)));
+  }
 };
 
 // fp8 "fnuz": the single NaN 0x80; a byte of d ^ 0x80808080 is zero.  Exact.
@@ -173,6 +206,16 @@ struct Chk<kChkFp8Eq> {
     one(v.w);
   }
   __device__ __forceinline__ bool flagged() const { return flag != 0; }
+  __device__ __forceinline__ void reset() { flag = 0; }
+  // Exact count: 0x80 in every byte of d ^ v4 that is zero (no borrow between
+  // bytes, unlike the any-zero test above).
+  __device__ __forceinline__ uint32_t zeros(uint32_t d) const {
+    const uint32_t t = d ^ v4;
+    return (uint32_t)__builtin_popcount(~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t | 0x7F7F7F7Fu));
+  }
+  __device__ __forceinline__ uint32_t exact(u32x4 v) const {
+    return zeros(v.x) + zeros(v.y) + zeros(v.z) + zeros(v.w);
+  }
 };
 
 // Element type of an item, resolved once per workgroup (or wave) into the
@@ -243,15 +286,22 @@ __device__ __forceinline__ void load_round(const unsigned char* body, uint32_t n
   }
 }
 
+struct NoRoundHook {
+  template <int U>
+  __device__ __forceinline__ void operator()(const u32x4 (&)[U]) const {}
+};
+
 // Streams the nvec aligned 16-byte vectors at `body` through consume(v):
 // round r holds vectors r*256*U .. r*256*U + 256*U - 1, lane t taking
 // vectors u*256 + t of each round.  Lanes past the end consume zero vectors.
-// With PIPE the loads of round r+1 are issued before round r is consumed
-// (two register sets, alternating), so a wave keeps loads in flight while it
-// computes.  Requires nvec > 0.  Returns the number of rounds (uniform over
-// the workgroup).
-template <int U, bool PIPE, class F>
-__device__ __forceinline__ uint32_t stream_body(const unsigned char* body, uint32_t nvec, F&& consume) {
+// After a round is consumed, done(v) sees the lane's U vectors of that round
+// while they are still in registers.  With PIPE the loads of round r+1 are
+// issued before round r is consumed (two register sets, alternating), so a
+// wave keeps loads in flight while it computes.  Requires nvec > 0.  Returns
+// the number of rounds (uniform over the workgroup).
+template <int U, bool PIPE, class F, class G = NoRoundHook>
+__device__ __forceinline__ uint32_t stream_body(const unsigned char* body, uint32_t nvec, F&& consume,
+                                                G&& done = G()) {
   constexpr uint32_t kRound = kBlock * U;
   const uint32_t full = nvec / kRound;
   const uint32_t rounds = full + ((nvec % kRound) ? 1u : 0u);
@@ -261,6 +311,7 @@ __device__ __forceinline__ uint32_t stream_body(const unsigned char* body, uint3
       load_round<U>(body, nvec, full, r, v);
 #pragma unroll
       for (int u = 0; u < U; ++u) consume(v[u]);
+      done(v);
     }
   } else {
     u32x4 va[U], vb[U];
@@ -270,14 +321,28 @@ __device__ __forceinline__ uint32_t stream_body(const unsigned char* body, uint3
       if (r + 1 < rounds) load_round<U>(body, nvec, full, r + 1, vb);
 #pragma unroll
       for (int u = 0; u < U; ++u) consume(va[u]);
+      done(va);
       if (++r == rounds) break;
       if (r + 1 < rounds) load_round<U>(body, nvec, full, r + 1, va);
 #pragma unroll
       for (int u = 0; u < U; ++u) consume(vb[u]);
+      done(vb);
       if (++r == rounds) break;
     }
   }
   return rounds;
+}
+
+// Exact NaN/Inf count (chk.exact) of a round's vectors when the lane's fast flag is set
+// (rare), then the flag is cleared for the next round.  The vectors are the
+// ones just loaded, so nothing is read again.
+template <int U, class C>
+__device__ __forceinline__ void count_flagged_round(C& chk, const u32x4 (&v)[U], uint32_t& count) {
+  if (chk.flagged()) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) count += chk.exact(v[u]);
+    chk.reset();
+  }
 }
 
 // Raw pattern of the ES-byte element at p.

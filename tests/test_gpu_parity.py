@@ -3,8 +3,8 @@
 Cases: sizes that span several work items and leave ragged heads and tails,
 misaligned starts (tensors carved from a byte buffer at every element-aligned
 offset), item sizes from 16 bytes to 4 MiB (the rows must not depend on how a
-tensor is split), random bit patterns with many NaN/Inf values (the exact
-recount path), large finite bf16 values that trip the packed fp16 pre-check,
+tensor is split), random bit patterns with many NaN/Inf values and every 16-bit pattern
+(the exact count of flagged rounds), large finite bf16 values that trip the packed fp16 pre-check,
 None and empty tensors, and the majority / diff kernels on random tables.
 """
 import numpy as np
@@ -104,7 +104,7 @@ def test_misaligned_clone_views_and_nonfinite_patterns():
 
 def test_large_finite_bf16_are_not_counted():
     # bf16 values with exponent 0xF8..0xFE look like fp16 NaN/Inf to the packed
-    # pre-check; the exact recount must not count them.
+    # pre-check; the exact count must not count them.
     g = gen(5)
     t = torch.empty(1 << 20, dtype=torch.bfloat16, device=DEV).normal_(0, 0.02, generator=g)
     iv = t.view(torch.int16)
@@ -115,6 +115,32 @@ def test_large_finite_bf16_are_not_counted():
     rows, plan = scan([t])
     assert_rows_equal(rows, oracle_rows([t]))
     assert int(rows[0, 3]) == 1
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_every_16bit_pattern_nan_dense(dtype):
+    # all 2^16 patterns (shuffled) in a tensor of several rounds per lane and in
+    # wave-item-sized slices: NaN/Inf in almost every lane's every round, so the
+    # exact count of flagged rounds runs everywhere
+    rng = np.random.default_rng(33)
+    pats = rng.permutation(1 << 16).astype(np.int64)
+    pats = np.where(pats >= 1 << 15, pats - (1 << 16), pats).astype(np.int16)
+    big = torch.from_numpy(np.tile(pats, 5)[:5 * 65536 - 3].copy()).to(DEV).view(dtype)
+    tensors = [big, big[1:]] + [big[k * 4096 + (k % 8):(k + 1) * 4096] for k in range(16)]
+    say(f"case every 16-bit pattern {dtype}")
+    rows, plan = scan(tensors)
+    assert_rows_equal(rows, oracle_rows(tensors))
+    counts, total = sdc.sdc_nonfinite(plan)
+    one = sdc.sdc_fingerprint_tensor(big)
+    torch.cuda.synchronize()
+    ref = oracle_nonfinite(tensors)
+    assert counts.cpu().numpy().astype(np.uint64).tolist() == ref.tolist()
+    assert int(total.item()) == int(ref.sum())
+    assert_rows_equal(sdc.rows_numpy(one), oracle_rows([big]))
+    # each copy of the 2^16 patterns holds 2^(16-E) with the E exponent bits all ones
+    mask = 0x7F80 if dtype == torch.bfloat16 else 0x7C00
+    dropped = sum(1 for p in pats[-3:] if int(p) & mask == mask)
+    assert int(rows[0, 3]) == 5 * (1 << (16 - bin(mask).count("1"))) - dropped
 
 
 def test_none_empty_and_many_tiny_tensors():
