@@ -240,6 +240,40 @@ def bench_recompute(args, torch, sdc, W_):
                 note="kernel_ms spans the step's 80 scan + compare launch pairs on the stream")
 
 
+def read_ceiling(args, torch, sdc, gib=32):
+    """Streaming-read reference in the same run: sdc_read_sum (the scan's load
+    structure, one add per 32-bit word, partial sums merged by a second launch)
+    over one `gib` GiB device buffer of random bits, timed with HIP events on
+    the launch stream.  Returns None when the device lacks the free memory."""
+    free, _ = torch.cuda.mem_get_info()
+    nbytes = gib << 30
+    if free < nbytes + (2 << 30):
+        log(f"bench: read ceiling skipped ({free / 2**30:.1f} GiB free)")
+        return None
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    out = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(sdc.sdc_read_sum_ws_bytes(nbytes), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        sdc.sdc_read_sum(buf, out=out, ws=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    log("bench: timing the streaming-read reference ...")
+    _, kms = time_steps(step, args.steps, args.warmup, stream)
+    del buf, ws
+    torch.cuda.empty_cache()
+    gbs = nbytes / kms / 1e6
+    return {"kernel": "read_sum_kernel (+ read_merge_kernel)", "bytes": nbytes, "kernel_ms": round(kms, 4),
+            "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "note": "sum of the 32-bit words of one buffer, read with the scan's load structure "
+                    "(1 MiB per workgroup, non-temporal 16-byte loads, partial sums merged "
+                    "by a second launch): the achievable streaming-read rate"}
+
+
 def cpu_baseline(w, out, budget_s, sdc, torch):
     """The oracle, single-threaded, on a bounded sample: whole tensors of the
     same list, in list order from layer 0, until the oracle has run budget_s
@@ -324,6 +358,7 @@ def main():
     total_bytes = plan.total_bytes
     achieved = total_bytes / kms / 1e6  # GB/s
     traffic = traffic_from_profile("llama70b_bf16")
+    ceiling = read_ceiling(args, torch, sdc)
     cpu = cpu_baseline(w, out, args.cpu_budget, sdc, torch) if args.cpu_budget > 0 else None
     value = total_bytes / ms / 1e6
     line = {
@@ -339,7 +374,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "fingerprint_kernel (+ merge_rows_kernel)",
-                     "kernel_ms": round(kms, 4), "kernel_hash": kernel_hash()},
+                     "kernel_ms": round(kms, 4), "kernel_hash": kernel_hash(),
+                     "frac_of_read_ceiling": (round(achieved / ceiling["gbs"], 4)
+                                              if ceiling else None)},
+        "read_ceiling": ceiling,
         "elements_per_s": round(plan.total_elems / ms * 1e3, 1),
         "plan_build_ms": plan_ms,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),

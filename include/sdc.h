@@ -339,6 +339,26 @@ int32_t sdc_confirm_verdict(const uint64_t* d_third, const uint64_t* d_self,
                             void* d_ws, uint64_t ws_bytes, int32_t* h_verdict,
                             sdc_stream_t stream);
 
+/* ---- measurement ----------------------------------------------------------- */
+
+/* Streaming-read reference (no passage of the pages defines it: it measures
+ * the bandwidth the fingerprint scan is read against).  *d_sum = the sum
+ * (mod 2^64) of the bytes/4 little-endian 32-bit words at d_buf, each
+ * zero-extended -- for an fp32 buffer, the same value as the sum column of its
+ * fingerprint.  The words are read with the scan's load structure (one
+ * workgroup per 1 MiB, non-temporal 16-byte loads, a partial sum per
+ * workgroup merged by a second one-workgroup launch) and one add per word, so
+ * the call's rate is the chip's streaming-read rate for that structure.
+ * d_buf: device memory, 16-byte aligned; bytes: a multiple of 4 (0 gives 0);
+ * d_ws: sdc_read_sum_ws_bytes(bytes) bytes of device memory, 8-byte aligned,
+ * caller-owned (no initial contents needed); d_sum: one device uint64_t.
+ * ASYNCHRONOUS on `stream`; calls that share d_ws must not overlap.
+ * Errors: SDC_ERR_INVALID (NULL, bytes % 4 != 0), SDC_ERR_ALIGN,
+ * SDC_ERR_WORKSPACE, SDC_ERR_RANGE, SDC_ERR_HIP. */
+int32_t sdc_read_sum_ws_bytes(uint64_t bytes, uint64_t* h_ws_bytes);
+int32_t sdc_read_sum(const void* d_buf, uint64_t bytes, void* d_ws, uint64_t ws_bytes,
+                     uint64_t* d_sum, sdc_stream_t stream);
+
 /* ---- misc ------------------------------------------------------------------ */
 
 /* Static text for a status code. */

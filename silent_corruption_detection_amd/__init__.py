@@ -22,7 +22,7 @@ __all__ = [
     "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
     "sdc_abi_version", "rows_numpy", "LIB_PATH", "sdc_ring_ws_bytes", "sdc_ring_compare",
     "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS", "sdc_sqnorm",
-    "sdc_tensor_ws_bytes", "sdc_fingerprint_tensor",
+    "sdc_tensor_ws_bytes", "sdc_fingerprint_tensor", "sdc_read_sum_ws_bytes", "sdc_read_sum",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
@@ -89,6 +89,8 @@ def _load():
         "sdc_ring_compare": [P, U32, U64, U32, P, U64, P, P],
         "sdc_ring_localize": [P, U32, U32, P, P],
         "sdc_confirm_verdict": [P, P, P, P, U64, P, U64, P, P],
+        "sdc_read_sum_ws_bytes": [U64, P],
+        "sdc_read_sum": [P, U64, P, U64, P, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -348,6 +350,32 @@ def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_AL
         ws.record_stream(s)
         for x in keep:
             x.record_stream(s)
+    return out
+
+
+def sdc_read_sum_ws_bytes(nbytes):
+    b = ctypes.c_uint64(0)
+    _check(_lib.sdc_read_sum_ws_bytes(nbytes, ctypes.byref(b)), "sdc_read_sum_ws_bytes")
+    return b.value
+
+
+def sdc_read_sum(buf, out=None, ws=None, stream=None):
+    """Sum mod 2^64 of the 32-bit words of the contiguous device tensor buf,
+    read at the chip's streaming rate, as an int64 [1] device tensor holding
+    the uint64 bit pattern (asynchronous).  ws: a reusable uint8 device
+    workspace of sdc_read_sum_ws_bytes(bytes) bytes (allocated when None)."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("sdc_read_sum needs a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=buf.device)
+    if not (out.is_cuda and out.dtype == torch.int64 and out.numel() >= 1 and out.device == buf.device):
+        raise ValueError("out must be an int64 device tensor on the buffer's device")
+    if ws is None:
+        ws = torch.empty(max(sdc_read_sum_ws_bytes(nbytes), 8), dtype=torch.uint8, device=buf.device)
+    _check(_lib.sdc_read_sum(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(ws.data_ptr()),
+                             ws.numel(), ctypes.c_void_p(out.data_ptr()),
+                             _stream_handle(stream, buf.device)), "sdc_read_sum")
     return out
 
 

@@ -11,8 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsdc.so")
-SOURCES = ["scan.hip", "tensor.hip", "nonfinite.hip", "norm.hip", "compare.hip", "plan.cpp",
-           "misc.cpp"]
+SOURCES = ["scan.hip", "tensor.hip", "nonfinite.hip", "norm.hip", "compare.hip", "readsum.hip",
+           "plan.cpp", "misc.cpp"]
 ARCH = os.environ.get("SDC_OFFLOAD_ARCH", "gfx950")
 
 

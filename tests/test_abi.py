@@ -168,3 +168,31 @@ def test_tensor_ws_bytes_errors(desc, item_bytes, code):
 def test_tensor_ws_bytes_empty_and_missing():
     assert tensor_ws_bytes((None, 100, 0, 0)) == (0, 32)
     assert tensor_ws_bytes((0x10000, 0, 2, 0)) == (0, 32)
+
+
+@pytest.mark.parametrize("buf,nbytes,ws,ws_bytes,out,code", [
+    (0x10000, 6, 0x30000, 8, 0x20000, -1),           # not a whole number of 32-bit words
+    (0x10000, 16, 0x30000, 8, None, -1),             # no output
+    (0x10000, 16, None, 8, 0x20000, -1),             # no workspace
+    (None, 16, 0x30000, 8, 0x20000, -1),             # no buffer
+    (0x10004, 16, 0x30000, 8, 0x20000, -3),          # buffer not 16-byte aligned
+    (0x10000, 16, 0x30004, 8, 0x20000, -3),          # workspace not 8-byte aligned
+    (0x10000, (1 << 20) + 16, 0x30000, 8, 0x20000, -4),   # two chunks need 16 bytes
+    (0x10000, 1 << 62, 0x30000, 8, 0x20000, -7)])    # more chunks than a grid holds
+def test_read_sum_argument_checks(buf, nbytes, ws, ws_bytes, out, code):
+    # every case returns before any HIP call (the pointers are never dereferenced)
+    import silent_corruption_detection_amd as sdc
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    V, U64 = ctypes.c_void_p, ctypes.c_uint64
+    lib.sdc_read_sum.argtypes = [V, U64, V, U64, V, V]
+    lib.sdc_read_sum.restype = ctypes.c_int32
+    assert lib.sdc_read_sum(buf, nbytes, ws, ws_bytes, out, None) == code
+
+
+def test_read_sum_ws_bytes():
+    import silent_corruption_detection_amd as sdc
+    MIB = 1 << 20
+    for nbytes, chunks in ((0, 1), (4, 1), (MIB, 1), (MIB + 4, 1), (MIB + 16, 2), (32 << 30, 32768)):
+        assert sdc.sdc_read_sum_ws_bytes(nbytes) == 8 * chunks
+    with pytest.raises(sdc.SdcError):
+        sdc.sdc_read_sum_ws_bytes(1 << 62)
