@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __res
                                                            sdc_row* __restrict__ partials,
                                                            uint64_t* __restrict__ counts,
                                                            uint64_t* __restrict__ total) {
-  const PlanItem it = items[blockIdx.x];
+  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
   uint32_t c = 0;
   dispatch_type(it.dtype_flags & ~kItemSigned,
                 [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type, U>(it); });

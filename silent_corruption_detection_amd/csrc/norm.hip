@@ -138,7 +138,7 @@ template <int U>
 __global__ void __launch_bounds__(kBlock) sqnorm_kernel(const PlanItem* __restrict__ items,
                                                         sdc_row* __restrict__ partials,
                                                         double* __restrict__ sq) {
-  const PlanItem it = items[blockIdx.x];
+  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
   double acc = 0.0;
   dispatch_dtype(it.dtype_flags, [&](auto dt) { acc = sq_item<decltype(dt), U>(it); });
   acc = block_sum_d(acc);

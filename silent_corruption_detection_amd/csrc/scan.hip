@@ -48,7 +48,7 @@ template <class Cfg>
 __global__ void __launch_bounds__(kBlock) fingerprint_kernel(const PlanItem* __restrict__ items,
                                                              sdc_row* __restrict__ partials,
                                                              sdc_row* __restrict__ out) {
-  const PlanItem it = items[blockIdx.x];
+  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
   Lane ln;
   dispatch_type(it.dtype_flags, [&](auto ty) { scan_item<decltype(ty), Cfg>(it, ln); });
   if (threadIdx.x != 0) return;
