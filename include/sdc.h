@@ -216,10 +216,15 @@ int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info, uint64_t*
 int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, double* d_sq,
                    double* d_total, uint32_t* d_flag, sdc_stream_t stream);
 
+/* Device workspace bytes of sdc_fingerprint on this list (the plan's size
+ * with the automatic item size: sdc_plan_bytes(h_tensors, n, 0)).  Host only;
+ * errors as sdc_plan_bytes. */
+int32_t sdc_fingerprint_ws_bytes(const sdc_tensor* h_tensors, uint64_t n, uint64_t* h_bytes);
+
 /* One-shot form of sdc_plan_build + sdc_fingerprint_plan: d_ws is a device
- * workspace of at least sdc_plan_bytes(h_tensors, n, 0) bytes that holds the
- * plan.  The plan upload is synchronous; the scan is asynchronous on stream.
- * The workspace must not be reused before the scan has completed. */
+ * workspace of at least sdc_fingerprint_ws_bytes(h_tensors, n) bytes that
+ * holds the plan.  The plan upload is synchronous; the scan is asynchronous
+ * on stream.  The workspace must not be reused before the scan has completed. */
 int32_t sdc_fingerprint(const sdc_tensor* h_tensors, uint64_t n, void* d_ws, uint64_t ws_bytes,
                         sdc_row* d_out, sdc_stream_t stream);
 

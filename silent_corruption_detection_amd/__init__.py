@@ -18,7 +18,7 @@ __all__ = [
     "F32", "BF16", "F16", "F64", "U8", "FP8_E4M3", "FP8_E5M2", "FP8_E4M3FNUZ", "FP8_E5M2FNUZ",
     "U16", "U32", "U64", "FLAG_SIGNED", "COL_SUM", "COL_WSUM", "COL_XOR", "COL_NONFINITE", "COL_ALL",
     "SdcError", "Plan", "sdc_plan_bytes", "sdc_plan_build", "sdc_fingerprint_plan",
-    "sdc_nonfinite", "sdc_fingerprint", "sdc_majority_ws_bytes", "sdc_majority_compare",
+    "sdc_nonfinite", "sdc_fingerprint", "sdc_fingerprint_ws_bytes", "sdc_majority_ws_bytes", "sdc_majority_compare",
     "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
     "sdc_abi_version", "rows_numpy", "LIB_PATH", "sdc_ring_ws_bytes", "sdc_ring_compare",
     "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS", "sdc_sqnorm",
@@ -77,6 +77,7 @@ def _load():
         "sdc_fingerprint_plan": [P, P, P, P],
         "sdc_nonfinite": [P, P, P, P, P],
         "sdc_fingerprint": [P, U64, P, U64, P, P],
+        "sdc_fingerprint_ws_bytes": [P, U64, P],
         "sdc_majority_ws_bytes": [U32, U64, P],
         "sdc_majority_compare": [P, U32, U64, U32, P, U64, P, P, P, P],
         "sdc_diff_ws_bytes": [U64, U64, P],
@@ -295,7 +296,8 @@ def sdc_fingerprint(tensors, out=None, stream=None, signed=False):
     if dev is None:
         dev = torch.device("cuda")
     nbytes = ctypes.c_uint64(0)
-    _check(_lib.sdc_plan_bytes(arr, len(tensors), 0, ctypes.byref(nbytes)), "sdc_plan_bytes")
+    _check(_lib.sdc_fingerprint_ws_bytes(arr, len(tensors), ctypes.byref(nbytes)),
+           "sdc_fingerprint_ws_bytes")
     ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=dev)
     out = _rows_out(out, len(tensors), dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
@@ -307,6 +309,16 @@ def sdc_fingerprint(tensors, out=None, stream=None, signed=False):
     for t in keep:
         t.record_stream(s)
     return out
+
+
+def sdc_fingerprint_ws_bytes(tensors, signed=False):
+    """Workspace bytes of sdc_fingerprint for this list of contiguous device
+    tensors (host only)."""
+    arr, _, _ = _descriptors(tensors, require_contiguous=True, signed=signed)
+    nbytes = ctypes.c_uint64(0)
+    _check(_lib.sdc_fingerprint_ws_bytes(arr, len(tensors), ctypes.byref(nbytes)),
+           "sdc_fingerprint_ws_bytes")
+    return nbytes.value
 
 
 def sdc_tensor_ws_bytes(t, item_bytes=0, signed=False):

@@ -139,6 +139,11 @@ extern "C" int32_t sdc_fingerprint_plan(const void* d_plan, const sdc_plan_info*
   return launch_scan(d_plan, h_info, d_out, as_stream(stream));
 }
 
+extern "C" int32_t sdc_fingerprint_ws_bytes(const sdc_tensor* h_tensors, uint64_t n,
+                                            uint64_t* h_bytes) {
+  return sdc_plan_bytes(h_tensors, n, 0, h_bytes);
+}
+
 extern "C" int32_t sdc_fingerprint(const sdc_tensor* h_tensors, uint64_t n, void* d_ws,
                                    uint64_t ws_bytes, sdc_row* d_out, sdc_stream_t stream) {
   sdc_plan_info info;

@@ -79,6 +79,21 @@ def test_plan_bytes_host_only():
     assert rc == 0
 
 
+def test_fingerprint_ws_bytes_is_the_automatic_plan_size():
+    import numpy as np
+    import silent_corruption_detection_amd as sdc
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    rng = np.random.default_rng(8)
+    for n in (0, 1, 7, 300, 5000):
+        descs = [(0x7F0000000000 + int(rng.integers(0, 1 << 20)) * 16, int(rng.integers(0, 3_000_000)),
+                  int(rng.integers(0, 3)), 0) for _ in range(n)]
+        arr = (_T * max(n, 1))(*[_T(*d) for d in descs])
+        out = ctypes.c_uint64(0)
+        assert lib.sdc_fingerprint_ws_bytes(arr, ctypes.c_uint64(n), ctypes.byref(out)) == 0
+        assert plan_bytes(descs) == (0, out.value)
+    assert lib.sdc_fingerprint_ws_bytes(None, ctypes.c_uint64(1), ctypes.byref(out)) == -1
+
+
 @pytest.mark.parametrize("desc,item_bytes,code", [
     ((0x10000, 10, 99, 0), 0, -2),     # unknown dtype
     ((0x10001, 10, 3, 0), 0, -3),      # fp64 pointer not 8-byte aligned
