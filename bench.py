@@ -287,7 +287,7 @@ def cpu_baseline(w, out, budget_s, sdc, torch):
     list: whole tensors in list order from layer 0.  First on one thread until
     it has run budget_s seconds; then on every usable host core at once (one
     oracle call per tensor per thread, ctypes releasing the GIL) over about
-    2 * budget_s seconds of CPU work in total.  Host copies are made first and
+    1.5 * budget_s seconds of CPU work in total.  Host copies are made first and
     not timed.  Every sampled row is checked against the GPU's."""
     import threading
     import numpy as np
@@ -318,7 +318,7 @@ def cpu_baseline(w, out, budget_s, sdc, torch):
     cores = usable_cores()
     # the same tensors again, so the threaded sample holds as many bytes as the
     # per-thread share of the CPU budget allows
-    per_thread = 2.0 * budget_s / cores
+    per_thread = 1.5 * budget_s / cores
     target = int(nbytes / spent * per_thread * cores)
     picked, tot = [], 0
     for k in order:
@@ -366,7 +366,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of single-threaded oracle work in the CPU baseline, and "
-                         "twice that in CPU seconds on all cores (0: skip)")
+                         "1.5 times that in CPU seconds on all cores (0: skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "recompute"],
                     help="c5 (default) prints the benchmark line; the others print their "
