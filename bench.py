@@ -270,8 +270,10 @@ def read_ceiling(args, torch, sdc, gib=32):
     return {"kernel": "read_sum_kernel (+ read_merge_kernel)", "bytes": nbytes, "kernel_ms": round(kms, 4),
             "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "note": "sum of the 32-bit words of one buffer, read with the scan's load structure "
-                    "(1 MiB per workgroup, non-temporal 16-byte loads, partial sums merged "
-                    "by a second launch): the achievable streaming-read rate"}
+                    "for lists of large items (1 MiB per workgroup, one workgroup per CU, "
+                    "non-pipelined rounds of non-temporal 16-byte loads, 8 per lane: the fastest "
+                    "depth for a pure read; partial sums merged by a second launch): the "
+                    "achievable streaming-read rate"}
 
 
 def usable_cores(cap=16):

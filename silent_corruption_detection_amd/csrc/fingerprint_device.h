@@ -155,6 +155,7 @@ struct BodyCfg {
 };
 typedef BodyCfg<4, true> DefaultBody;  // ~106 VGPRs: 4 workgroups per CU
 typedef BodyCfg<8, true> DeepBody;     // ~188 VGPRs: deeper pipeline, 2 workgroups per CU
+typedef BodyCfg<kWideU, false> WideBody;  // the wide shape: one workgroup per CU
 // Plans whose items average at least this many bytes use DeepBody (measured:
 // better for items of ~170 KiB and more, worse for lists of small tensors).
 constexpr uint64_t kDeepItemBytes = 96ull << 10;

@@ -12,7 +12,7 @@ namespace sdc {
 namespace {
 
 // ---- NaN/Inf count only ----------------------------------------------------------
-template <class Ty, int U>
+template <class Ty, int U, bool PIPE>
 __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
   constexpr uint32_t es = Ty::ES;
   const uint32_t t = threadIdx.x;
@@ -26,7 +26,7 @@ __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
     if (sp.nvec) {
       const unsigned char* body = sp.base + (uint64_t)sp.h * es;
       Chk<Ty::CHK> chk(rule);
-      stream_body<U, true>(body, sp.nvec, [&](u32x4 v) { chk.add(v); },
+      stream_body<U, PIPE>(body, sp.nvec, [&](u32x4 v) { chk.add(v); },
                            [&](const u32x4 (&v)[U]) { count_flagged_round(chk, v, c); });
     }
   }
@@ -47,7 +47,7 @@ struct Unsigned {
   typedef TypeTag<Ty::ES, false, Ty::CHK> type;
 };
 
-template <int U>
+template <int U, bool PIPE>
 __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __restrict__ items,
                                                            sdc_row* __restrict__ partials,
                                                            uint64_t* __restrict__ counts,
@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __res
   const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
   uint32_t c = 0;
   dispatch_type(it.dtype_flags & ~kItemSigned,
-                [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type, U>(it); });
+                [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type, U, PIPE>(it); });
   if (threadIdx.x != 0) return;
   if (counts) {
     if (it.dtype_flags & kItemWhole) counts[it.row] = c;
@@ -151,12 +151,20 @@ extern "C" int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info
     if ((st = launch_status())) return st;
   }
   if (n_block) {
-    if (h_info->total_bytes / h_info->n_items >= kCheckDeepItemBytes)
-      hipLaunchKernelGGL(nonfinite_kernel<kCheckDeepU>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
-                         v.items, v.partials, d_counts, d_total);
-    else
-      hipLaunchKernelGGL(nonfinite_kernel<kCheckU>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
-                         v.items, v.partials, d_counts, d_total);
+    const dim3 grid((uint32_t)n_block), block(kBlock);
+    switch (item_shape(h_info->total_bytes, h_info->n_items, kCheckDeepItemBytes)) {
+      case kShapeWide:
+        hipLaunchKernelGGL((nonfinite_kernel<kWideU, false>), grid, block, kWideLdsBytes, s, v.items,
+                           v.partials, d_counts, d_total);
+        break;
+      case kShapeDeep:
+        hipLaunchKernelGGL((nonfinite_kernel<kCheckDeepU, true>), grid, block, 0, s, v.items,
+                           v.partials, d_counts, d_total);
+        break;
+      default:
+        hipLaunchKernelGGL((nonfinite_kernel<kCheckU, true>), grid, block, 0, s, v.items, v.partials,
+                           d_counts, d_total);
+    }
     if ((st = launch_status())) return st;
   }
   if (d_counts && h_info->n_split) {

@@ -113,7 +113,7 @@ __device__ __forceinline__ double block_sum_d(double v) {
   return all;
 }
 
-template <class Dt, int U>
+template <class Dt, int U, bool PIPE>
 __device__ __forceinline__ double sq_item(const PlanItem& it) {
   constexpr uint32_t DT = Dt::DTYPE, es = dt_size<DT>();
   const Span sp = span_of<es>(it);
@@ -127,20 +127,21 @@ __device__ __forceinline__ double sq_item(const PlanItem& it) {
     const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + t - 128u) * es));
     acc = __builtin_fma(y, y, acc);
   }
-  // lane t adds its vectors t, t + 256, t + 512, ... in that order
+  // lane t adds its vectors t, t + 256, t + 512, ... in that order, whatever
+  // the round depth and pipelining
   if (sp.nvec)
-    stream_body<U, true>(sp.base + (uint64_t)sp.h * es, sp.nvec,
-                               [&](u32x4 v) { acc = sq_vec<DT>(v, acc); });
+    stream_body<U, PIPE>(sp.base + (uint64_t)sp.h * es, sp.nvec,
+                         [&](u32x4 v) { acc = sq_vec<DT>(v, acc); });
   return acc;
 }
 
-template <int U>
+template <int U, bool PIPE>
 __global__ void __launch_bounds__(kBlock) sqnorm_kernel(const PlanItem* __restrict__ items,
                                                         sdc_row* __restrict__ partials,
                                                         double* __restrict__ sq) {
   const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
   double acc = 0.0;
-  dispatch_dtype(it.dtype_flags, [&](auto dt) { acc = sq_item<decltype(dt), U>(it); });
+  dispatch_dtype(it.dtype_flags, [&](auto dt) { acc = sq_item<decltype(dt), U, PIPE>(it); });
   acc = block_sum_d(acc);
   if (threadIdx.x != 0) return;
   if (it.dtype_flags & kItemWhole) sq[it.row] = acc;
@@ -253,12 +254,20 @@ extern "C" int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, d
     if ((st = launch_status())) return st;
   }
   if (n_block) {
-    if (h_info->total_bytes / h_info->n_items >= kCheckDeepItemBytes)
-      hipLaunchKernelGGL(sqnorm_kernel<kCheckDeepU>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
-                         v.items, v.partials, d_sq);
-    else
-      hipLaunchKernelGGL(sqnorm_kernel<kCheckU>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
-                         v.items, v.partials, d_sq);
+    const dim3 grid((uint32_t)n_block), block(kBlock);
+    switch (item_shape(h_info->total_bytes, h_info->n_items, kCheckDeepItemBytes)) {
+      case kShapeWide:
+        hipLaunchKernelGGL((sqnorm_kernel<kWideU, false>), grid, block, kWideLdsBytes, s, v.items,
+                           v.partials, d_sq);
+        break;
+      case kShapeDeep:
+        hipLaunchKernelGGL((sqnorm_kernel<kCheckDeepU, true>), grid, block, 0, s, v.items, v.partials,
+                           d_sq);
+        break;
+      default:
+        hipLaunchKernelGGL((sqnorm_kernel<kCheckU, true>), grid, block, 0, s, v.items, v.partials,
+                           d_sq);
+    }
     if ((st = launch_status())) return st;
   }
   if (h_info->n_split) {

@@ -1,14 +1,18 @@
 // readsum.hip -- the streaming-read reference kernel, for gfx950.
 //
-// Sums the 32-bit words of one buffer, read exactly as the fingerprint scan
-// reads the body of a work item (one workgroup per 1 MiB chunk, pipelined
-// rounds of 8 non-temporal 16-byte loads per lane), with one add per word in
-// place of the fingerprint's arithmetic.  Like the scan's split tensors, each
-// workgroup writes a partial result and a second launch merges them (a single
-// shared atomic per workgroup instead costs about 15 % of the rate: every
-// workgroup's update of one address is serialised across the XCDs).  Its rate
-// is the streaming-read bandwidth the chip reaches with that load structure,
-// the ceiling against which the scans' bandwidth is read.
+// Sums the 32-bit words of one buffer, read the way the fingerprint scan reads
+// the body of a work item of a list of large items (one workgroup per 1 MiB
+// chunk, one workgroup per CU, non-pipelined rounds of non-temporal 16-byte
+// loads), with one add per word in place of the fingerprint's arithmetic.
+// Its rounds hold 8 loads per lane instead of the scan's 12: with nothing to
+// compute between rounds, 8 is the fastest depth measured (7.41-7.42 TB/s
+// over 32 GiB, against 7.31 with 12 and 7.28 with pipelined rounds).  Like
+// the scan's split tensors, each workgroup writes a partial result and a
+// second launch merges them (a single shared atomic per workgroup instead
+// costs about 15 % of the rate: every workgroup's update of one address is
+// serialised across the XCDs).  Its rate is the streaming-read bandwidth the
+// chip reaches with that load structure, the ceiling against which the scans'
+// bandwidth is read.
 #include "scan_device.h"
 
 namespace sdc {
@@ -31,7 +35,7 @@ __global__ void __launch_bounds__(kBlock)
   const uint32_t nv = (uint32_t)min<uint64_t>(nvec - v0, kReadChunkVecs);
   uint64_t s = 0;
   if (nv) {
-    stream_body<kReadU, true>(buf + v0 * kVecBytes, nv, [&](u32x4 v) {
+    stream_body<kReadU, false>(buf + v0 * kVecBytes, nv, [&](u32x4 v) {
       s += (uint64_t)v.x + (uint64_t)v.y + (uint64_t)v.z + (uint64_t)v.w;
     });
   }
@@ -99,7 +103,7 @@ extern "C" int32_t sdc_read_sum(const void* d_buf, uint64_t bytes, void* d_ws, u
   const uint64_t chunks = read_chunks(bytes);
   hipStream_t s = as_stream(stream);
   uint64_t* partial = static_cast<uint64_t*>(d_ws);
-  hipLaunchKernelGGL(read_sum_kernel, dim3((uint32_t)chunks), dim3(kBlock), 0, s,
+  hipLaunchKernelGGL(read_sum_kernel, dim3((uint32_t)chunks), dim3(kBlock), kWideLdsBytes, s,
                      static_cast<const unsigned char*>(d_buf), bytes / kVecBytes,
                      (uint32_t)((bytes % kVecBytes) / 4u), partial);
   if ((st = launch_status())) return st;

@@ -14,7 +14,9 @@
 //     tensor can have a misaligned head and only the last one a tail.
 //   * The aligned body is read with coalesced 16-byte non-temporal buffer
 //     loads (lane t of the workgroup takes vector 256*it + t of the body),
-//     U per lane in flight.
+//     U per lane in flight.  Lists of large items (>= 512 KiB on average) run
+//     one workgroup per CU with 12 loads per lane per round; lists of smaller
+//     items run 2-4 workgroups per CU with pipelined rounds.
 //   * Per lane the 16-bit path keeps 32-bit partial sums built with
 //     v_dot2_u32_u16 (two elements per instruction): A = sum x,
 //     C = sum (k x) with k the element's slot in its 8-element vector, and a
@@ -110,12 +112,19 @@ int32_t launch_scan(const void* d_plan, const sdc_plan_info* h, sdc_row* out, hi
     if ((st = launch_status())) return st;
   }
   if (n_block) {
-    if (h->total_bytes / h->n_items >= kDeepItemBytes)
-      hipLaunchKernelGGL(fingerprint_kernel<DeepBody>, dim3((uint32_t)n_block), dim3(kBlock), 0, s,
-                         v.items, v.partials, out);
-    else
-      hipLaunchKernelGGL(fingerprint_kernel<DefaultBody>, dim3((uint32_t)n_block), dim3(kBlock), 0,
-                         s, v.items, v.partials, out);
+    const dim3 grid((uint32_t)n_block), block(kBlock);
+    switch (item_shape(h->total_bytes, h->n_items, kDeepItemBytes)) {
+      case kShapeWide:
+        hipLaunchKernelGGL(fingerprint_kernel<WideBody>, grid, block, kWideLdsBytes, s, v.items,
+                           v.partials, out);
+        break;
+      case kShapeDeep:
+        hipLaunchKernelGGL(fingerprint_kernel<DeepBody>, grid, block, 0, s, v.items, v.partials, out);
+        break;
+      default:
+        hipLaunchKernelGGL(fingerprint_kernel<DefaultBody>, grid, block, 0, s, v.items, v.partials,
+                           out);
+    }
     if ((st = launch_status())) return st;
   }
   if (h->n_split) {

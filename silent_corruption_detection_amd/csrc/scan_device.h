@@ -262,6 +262,31 @@ constexpr int kCheckU = 8;
 constexpr int kCheckDeepU = 16;
 constexpr uint64_t kCheckDeepItemBytes = 96ull << 10;
 
+// "Wide" launch shape of every scan-family kernel for plans whose items
+// average at least kWideItemBytes: kWideU vectors per lane per round, not
+// pipelined (a wave issues a round's loads, waits for them and consumes
+// them), and one workgroup per CU.  The launch reserves kWideLdsBytes of
+// dynamic LDS that no kernel touches: a CU has 160 KiB, so a second
+// workgroup never fits.  HBM streams best with about 8-12 MiB of reads in
+// flight over the chip; the default shapes (2-4 workgroups per CU, pipelined
+// rounds) keep more than that outstanding and lose 4-5 % to it.  Measured on
+// the 141 GB Llama-70B bf16 list (1 MiB items, median of 10 scans, one box):
+// this shape 7.46 TB/s, two workgroups per CU with pipelined 8-vector rounds
+// (the shape used below the threshold) 7.13; 10 / 14 / 16 vectors per round
+// 7.40 / 7.39 / 7.41; pipelined rounds at one workgroup per CU 7.29.  With
+// 128 KiB items one workgroup per CU loses 25 % (each item's start-up
+// latency is then exposed), hence the threshold.
+constexpr int kWideU = 12;
+constexpr uint64_t kWideItemBytes = 512ull << 10;
+constexpr uint32_t kWideLdsBytes = 96u << 10;
+
+// Launch shape of a plan's workgroup items from their average size.
+enum ItemShape : int { kShapeShort = 0, kShapeDeep = 1, kShapeWide = 2 };
+inline int item_shape(uint64_t total_bytes, uint64_t n_items, uint64_t deep_bytes) {
+  const uint64_t avg = n_items ? total_bytes / n_items : 0;
+  return avg >= kWideItemBytes ? kShapeWide : (avg >= deep_bytes ? kShapeDeep : kShapeShort);
+}
+
 // Loads round r (vectors r*256*U .. of the body) into v.  Rounds below
 // `full` are complete; the last, partial round masks lanes past the end,
 // whose vectors then read as zero.
