@@ -102,6 +102,55 @@ def test_misaligned_clone_views_and_nonfinite_patterns():
     assert int(total.item()) == int(ref.sum())
 
 
+def test_launch_shapes_rows_counts_and_norms():
+    # A plan's workgroup items run in one of three launch shapes chosen by the
+    # average item size: short (< 96 KiB), deep (96-512 KiB) and wide (>= 512 KiB:
+    # one workgroup per CU, non-pipelined rounds of 12 vectors per lane).  Rows,
+    # NaN/Inf counts and squared norms equal the oracle's in every shape, with
+    # sparse NaN/Inf (every class, misaligned heads, ragged tails) and with random
+    # bits (one element in 256 is NaN/Inf, and one in 32 trips the packed fp16
+    # pre-check, so most lanes' rounds are counted exactly).
+    from _util import assert_sq_close, oracle_sqnorms
+    specials = {4: [0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001, 0xFFFFFFFF],
+                2: [0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0xFFFF]}
+    rng = np.random.default_rng(31)
+    tensors = []
+    for dtype, off, n in ((torch.float32, 0, 6_000_000), (torch.bfloat16, 2, 5_000_003),
+                          (torch.float16, 6, 3_000_001)):
+        es = ES[dtype]
+        buf = torch.zeros(n * es + 16, dtype=torch.uint8, device=DEV)
+        t = carve(buf, off, n, dtype)
+        t.normal_(0, 0.02, generator=gen(n))
+        iv = t.view(torch.int32 if es == 4 else torch.int16)
+        pos = sorted(set([0, n - 1] + rng.integers(0, n, size=40).tolist()))
+        pats = specials[es] if dtype != torch.float16 else [0x7C00, 0xFC00, 0x7E00, 0x7C01, 0xFFFF]
+        for j, p in enumerate(pos):
+            v = pats[j % len(pats)]
+            iv[p] = v - (1 << (8 * es)) if v >= 1 << (8 * es - 1) else v
+        tensors.append(t)
+    tensors.append(random_bits(2 * 2_000_005, seed=77).view(torch.bfloat16))
+    ref_rows = oracle_rows(tensors)
+    ref_nf = oracle_nonfinite(tensors)
+    ref_sq = oracle_sqnorms(tensors)
+    numels = [t.numel() for t in tensors]
+    assert int(ref_nf[3]) > 5_000  # the random-bits tensor: about 2M / 256 NaN/Inf
+    for ib, want in ((65536, "short"), (256 << 10, "deep"), (1 << 20, "wide"), (4 << 20, "wide")):
+        plan = sdc.sdc_plan_build(tensors, item_bytes=ib)
+        avg = plan.total_bytes // plan.n_items
+        shape = "wide" if avg >= 512 << 10 else ("deep" if avg >= 96 << 10 else "short")
+        assert shape == want, (ib, avg)
+        say(f"case launch shape {shape} item_bytes={ib}")
+        out = sdc.sdc_fingerprint_plan(plan)
+        counts, total = sdc.sdc_nonfinite(plan)
+        sq, sq_total, flag = sdc.sdc_sqnorm(plan)
+        torch.cuda.synchronize()
+        assert_rows_equal(sdc.rows_numpy(out), ref_rows)
+        assert counts.cpu().numpy().astype(np.uint64).tolist() == ref_nf.tolist()
+        assert int(total.item()) == int(ref_nf.sum())
+        assert_sq_close(sq.cpu().tolist(), ref_sq, numels)
+        assert int(flag.item()) == 1
+
+
 def test_large_finite_bf16_are_not_counted():
     # bf16 values with exponent 0xF8..0xFE look like fp16 NaN/Inf to the packed
     # pre-check; the exact count must not count them.
