@@ -31,17 +31,6 @@ constexpr uint64_t kAutoMin = 64ull << 10;
 constexpr uint64_t kAutoMax = 1ull << 20;
 constexpr uint64_t kMaxGrid = 0x7FFFFFFFull;
 
-// Automatic item size of the single-tensor scan: about kTensorTargetItems
-// items (four per CU), same bounds.  Measured on 512 MiB bf16 tensors: 64 KiB
-// items 5.7 TB/s, 256 KiB 6.5, 512 KiB - 2 MiB 6.5-6.6, 4 MiB 5.6.
-constexpr uint64_t kTensorTargetItems = 1024;
-inline uint64_t tensor_item_bytes(uint64_t bytes) {
-  uint64_t ib = bytes / kTensorTargetItems;
-  ib = (ib < 1 ? 1 : ib);
-  ib = (ib + 4095) / 4096 * 4096;
-  return ib < kAutoMin ? kAutoMin : (ib > kAutoMax ? kAutoMax : ib);
-}
-
 constexpr uint64_t kPlanMagic = 0x31766E6163534453ull;  // "SDScanv1", little-endian
 
 // Wave items: small tensors scanned whole by a group of 64 >> c lanes of a

@@ -149,7 +149,9 @@ def one_tensor_plan_items(desc, item_bytes):
 
 
 DESCS = [(0x10000, 1, 0, 0), (0x10004, 1000, 0, 0), (0x10002, 3 << 20, 1, 0),
-         (0x10000, 5 << 30, 1, 1), (0x10008, 12345678, 3, 0), (0x10003, 7777777, 4, 0)]
+         (0x10000, 5 << 30, 1, 1), (0x10008, 12345678, 3, 0), (0x10003, 7777777, 4, 0),
+         (0x10000, (64 << 20) - 1, 1, 0), (0x10002, 64 << 20, 2, 0), (0x10004, 300 << 20, 0, 0),
+         (0x10001, (1 << 30) + 7, 4, 0)]
 
 
 @pytest.mark.parametrize("desc", DESCS)
@@ -163,13 +165,28 @@ def test_tensor_ws_bytes_match_the_plan_split(desc, item_bytes):
     assert ws == 32 * one_tensor_plan_items(desc, item_bytes)[0]
 
 
+def auto_tensor_item_bytes(nbytes):
+    # tensors of at least 128 MiB: a multiple of 256 items (one per CU per pass)
+    # of at most 4 MiB; smaller ones: about 1024 items within [64 KiB, 1 MiB];
+    # item sizes are multiples of 4 KiB
+    r4k = lambda b: -(-b // 4096) * 4096
+    if nbytes >= 128 << 20:
+        passes = -(-nbytes // (256 * (4 << 20)))
+        return r4k(-(-nbytes // (256 * passes)))
+    return min(max(r4k(max(nbytes // 1024, 1)), 64 << 10), 1 << 20)
+
+
 @pytest.mark.parametrize("desc", DESCS)
 def test_tensor_automatic_item_size(desc):
-    # about 1024 items, a multiple of 4 KiB within [64 KiB, 1 MiB]
-    nbytes = one_tensor_plan_items(desc, 65536)[1]
-    ib = -(-max(nbytes // 1024, 1) // 4096) * 4096
-    ib = min(max(ib, 64 << 10), 1 << 20)
-    assert tensor_ws_bytes(desc)[1] == 32 * one_tensor_plan_items(desc, ib)[0]
+    nbytes = desc[1] * {0: 4, 1: 2, 2: 2, 3: 8, 4: 1}[desc[2]]
+    ib = auto_tensor_item_bytes(nbytes)
+    assert ib % 4096 == 0 and ib <= 4 << 20
+    n_items, total = one_tensor_plan_items(desc, ib)
+    assert total == nbytes
+    assert tensor_ws_bytes(desc)[1] == 32 * n_items
+    if nbytes >= 128 << 20:  # one item per CU per pass, at most 4 MiB each
+        passes = -(-nbytes // (256 * (4 << 20)))
+        assert 256 * passes - 256 < n_items <= 256 * passes
 
 
 @pytest.mark.parametrize("desc,item_bytes,code", [

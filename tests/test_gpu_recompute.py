@@ -75,6 +75,21 @@ def test_tensor_rows_do_not_depend_on_the_item_size():
             assert_rows_equal(sdc.rows_numpy(r), ref)
 
 
+def test_tensor_automatic_split_around_128_mib():
+    # tensors of at least 128 MiB are cut into one item per CU (the tensor-wide
+    # launch shape), smaller ones into about 1024 items: rows equal the oracle's
+    # on both sides of the threshold, with misaligned starts and ragged tails
+    g = gen(7)
+    for dtype, nbytes, off in ((torch.float32, 128 << 20, 4), (torch.float32, (128 << 20) - 4, 0),
+                               (torch.bfloat16, 300 << 20, 6), (torch.uint8, (128 << 20) + 1, 3)):
+        es = torch.empty(0, dtype=dtype).element_size()
+        buf = torch.randint(0, 256, (nbytes + 16,), dtype=torch.uint8, device=DEV, generator=g)
+        t = carve(buf, off, nbytes // es, dtype)
+        say(f"case tensor automatic split dtype={dtype} bytes={nbytes} off={off}")
+        assert_rows_equal(one_row(t), oracle_rows([t]))
+        del buf, t
+
+
 def test_tensor_empty_missing_and_large():
     assert one_row(torch.empty(0, device=DEV)).tolist() == [[0, 0, 0, 0]]
     # a 2 GiB bf16 tensor (the Llama-70B embedding's size) equals the list scan's row
