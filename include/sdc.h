@@ -92,7 +92,7 @@ enum {
  *   ptr    device pointer to numel contiguous elements (row-major, little-
  *          endian), aligned to the element size; NULL means a missing tensor
  *          (its row is all zero, [BLOG] "Compare by fingerprint").
- *   numel  number of elements (0 gives a zero row); below 2^62.
+ *   numel  number of elements (0 gives a zero row); numel * element size below 2^62.
  *   dtype  one of the SDC_* element types above.
  *   flags  0 or SDC_FLAG_SIGNED. */
 typedef struct {
@@ -276,13 +276,14 @@ int32_t sdc_majority_ws_bytes(uint32_t R, uint64_t T, uint64_t* h_bytes);
  *   d_ws       sdc_majority_ws_bytes(R, T) bytes of device workspace.
  * SYNCHRONOUS (waits for stream).  R == 1 never diverges.
  * Errors: SDC_ERR_INVALID (R == 0, T == 0, NULL, bad mask), SDC_ERR_WORKSPACE,
- * SDC_ERR_HIP. */
+ * SDC_ERR_RANGE (R * T too large, or the R-byte host staging buffer could not
+ * be allocated; nothing is queued then), SDC_ERR_HIP. */
 int32_t sdc_majority_compare(const sdc_row* d_table, uint32_t R, uint64_t T, uint32_t col_mask,
                              void* d_ws, uint64_t ws_bytes, sdc_majority* h_res,
                              uint8_t* h_suspect, uint8_t* d_tensor_status, sdc_stream_t stream);
 
 /* Device workspace bytes for sdc_fingerprint_diff over T rows reporting up to
- * idx_cap indices. */
+ * idx_cap indices (an idx_cap above T counts as T: at most T rows differ). */
 int32_t sdc_diff_ws_bytes(uint64_t T, uint64_t idx_cap, uint64_t* h_bytes);
 
 /* [BLOG] "Check 2" (replay vs original) and the check after a restore:
@@ -293,7 +294,9 @@ int32_t sdc_diff_ws_bytes(uint64_t T, uint64_t idx_cap, uint64_t* h_bytes);
  *             flip localisation: when X_a ^ X_b = 2^b, S_b - S_a = s * 2^b and
  *             W_b - W_a = s * (i+1) * 2^b with one sign s = +-1 and
  *             (i+1) * 2^b < 2^63, the change is one flip of bit b of element i.
- * SYNCHRONOUS.  Errors: SDC_ERR_INVALID, SDC_ERR_WORKSPACE, SDC_ERR_HIP. */
+ * SYNCHRONOUS.  Errors: SDC_ERR_INVALID, SDC_ERR_WORKSPACE, SDC_ERR_RANGE (T or
+ * idx_cap >= 2^58, or the host staging of min(idx_cap, T) records could not be
+ * allocated; nothing is queued then), SDC_ERR_HIP. */
 int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, uint64_t T, uint32_t col_mask,
                              void* d_ws, uint64_t ws_bytes, uint64_t* h_n_diff, uint64_t* h_idx,
                              uint64_t idx_cap, sdc_flip_hint* h_hints, sdc_stream_t stream);
@@ -319,7 +322,8 @@ int32_t sdc_ring_compare(const uint64_t* d_table, uint32_t n, uint64_t width, ui
 /* Host-only (no HIP call).  h_culprit[q] = 1 for every rank q that appears,
  * as target or replayer, in at least two mismatched pairs; h_ambiguous[r] = 1
  * for every mismatched pair r that contains no culprit (it needs
- * confirmation).  Errors: SDC_ERR_INVALID. */
+ * confirmation).  Errors: SDC_ERR_INVALID, SDC_ERR_RANGE (the n-entry host
+ * work array could not be allocated). */
 int32_t sdc_ring_localize(const uint8_t* h_mismatch, uint32_t n, uint32_t offset,
                           uint8_t* h_culprit, uint8_t* h_ambiguous);
 

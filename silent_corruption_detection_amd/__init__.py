@@ -161,6 +161,28 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _same_device(a, b):
+    return a.type == b.type and (a.index is None or b.index is None or a.index == b.index)
+
+
+def _arg(t, name, dtype, numel, device):
+    """A caller-supplied tensor the library reads or writes through a device
+    pointer: it must be a contiguous `dtype` tensor of at least `numel`
+    elements on `device` (a host tensor's address handed to a kernel would
+    fault the GPU; a short one would be written past its end)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or not _same_device(t.device, device):
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+    return t
+
+
 # sdc_tensor as a numpy record: the descriptor table is filled column by
 # column (a per-tensor ctypes struct costs ~1 us, too slow for 10^5 tensors).
 _DESC = np.dtype([("ptr", "<u8"), ("numel", "<u8"), ("dtype", "<u4"), ("flags", "<u4")])
@@ -263,9 +285,7 @@ def sdc_plan_build(tensors, item_bytes=0, device=None, stream=None, signed=False
 def _rows_out(out, n, device):
     if out is None:
         return torch.empty((max(n, 0), 4), dtype=torch.int64, device=device)
-    if out.dtype != torch.int64 or out.numel() < 4 * n or not out.is_contiguous():
-        raise ValueError("out must be a contiguous int64 tensor with n*4 elements")
-    return out
+    return _arg(out, "out", torch.int64, 4 * n, device)
 
 
 def sdc_fingerprint_plan(plan, out=None, stream=None):
@@ -284,6 +304,8 @@ def sdc_nonfinite(plan, counts=None, total=None, stream=None):
         counts = torch.empty(max(plan.n_tensors, 1), dtype=torch.int64, device=plan.device)
     if total is None:
         total = torch.empty(1, dtype=torch.int64, device=plan.device)
+    _arg(counts, "counts", torch.int64, plan.n_tensors, plan.device)
+    _arg(total, "total", torch.int64, 1, plan.device)
     _check(_lib.sdc_nonfinite(ctypes.c_void_p(plan.buf.data_ptr()), ctypes.byref(plan.info),
                               ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(total.data_ptr()),
                               _stream_handle(stream, plan.device)), "sdc_nonfinite")
@@ -341,15 +363,17 @@ def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_AL
         dev = torch.device("cuda")
     nb = ctypes.c_uint64(0)
     _check(_lib.sdc_tensor_ws_bytes(arr, item_bytes, ctypes.byref(nb)), "sdc_tensor_ws_bytes")
+    if ws is not None:
+        _arg(ws, "ws", torch.uint8, 0, dev)
     if ws is None or ws.numel() < nb.value:
         ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
     out = _rows_out(out, 1, dev)
     ref_p = mis_p = None
     if ref is not None:
-        if ref.dtype != torch.int64 or ref.numel() < 4 or not ref.is_contiguous():
-            raise ValueError("ref must be a contiguous int64 row (4 elements)")
-        if mismatch is None or mismatch.dtype != torch.int32 or mismatch.numel() < 1:
+        _arg(ref, "ref", torch.int64, 4, dev)
+        if mismatch is None:
             raise ValueError("a compare needs a one-element int32 mismatch counter")
+        _arg(mismatch, "mismatch", torch.int32, 1, dev)
         ref_p, mis_p = ref.data_ptr(), mismatch.data_ptr()
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     _check(_lib.sdc_fingerprint_tensor(arr, item_bytes, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
@@ -381,10 +405,10 @@ def sdc_read_sum(buf, out=None, ws=None, stream=None):
     nbytes = buf.numel() * buf.element_size()
     if out is None:
         out = torch.empty(1, dtype=torch.int64, device=buf.device)
-    if not (out.is_cuda and out.dtype == torch.int64 and out.numel() >= 1 and out.device == buf.device):
-        raise ValueError("out must be an int64 device tensor on the buffer's device")
+    _arg(out, "out", torch.int64, 1, buf.device)
     if ws is None:
         ws = torch.empty(max(sdc_read_sum_ws_bytes(nbytes), 8), dtype=torch.uint8, device=buf.device)
+    _arg(ws, "ws", torch.uint8, 0, buf.device)  # its size is checked by the library
     _check(_lib.sdc_read_sum(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(ws.data_ptr()),
                              ws.numel(), ctypes.c_void_p(out.data_ptr()),
                              _stream_handle(stream, buf.device)), "sdc_read_sum")
@@ -408,17 +432,15 @@ def sdc_majority_compare(table, R, T=None, col_mask=COL_ALL, tensor_status=None,
     ("suspects", None when some tensor has no strict majority) and flags."""
     if T is None:
         T = table.shape[0] // R
-    if table.dtype != torch.int64 or not table.is_contiguous() or table.numel() < R * T * 4:
-        raise ValueError("table must be a contiguous int64 [R*T, 4] device tensor")
     dev = table.device
+    _arg(table, "table", torch.int64, R * T * 4, dev)
+    st_ptr = None
+    if tensor_status is not None:
+        _arg(tensor_status, "tensor_status", torch.uint8, T, dev)
+        st_ptr = ctypes.c_void_p(tensor_status.data_ptr())
     ws = _sync_ws(sdc_majority_ws_bytes(R, T), dev)
     res = _Majority()
     sus = (ctypes.c_uint8 * max(R, 1))()
-    st_ptr = None
-    if tensor_status is not None:
-        if tensor_status.dtype != torch.uint8 or tensor_status.numel() < T:
-            raise ValueError("tensor_status must be a uint8 device tensor of T elements")
-        st_ptr = ctypes.c_void_p(tensor_status.data_ptr())
     _check(_lib.sdc_majority_compare(ctypes.c_void_p(table.data_ptr()), R, T, col_mask,
                                      ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.byref(res),
                                      sus, st_ptr, _stream_handle(stream, dev)),
@@ -445,8 +467,10 @@ def sdc_fingerprint_diff(a, b, col_mask=COL_ALL, idx_cap=None, hints=True, strea
     if not (a.is_contiguous() and b.is_contiguous()):
         raise ValueError("a and b must be contiguous")
     T = a.shape[0]
-    cap = T if idx_cap is None else idx_cap
+    cap = T if idx_cap is None else min(idx_cap, T)  # at most T rows differ
     dev = a.device
+    _arg(a, "a", torch.int64, 0, dev)
+    _arg(b, "b", torch.int64, 0, dev)
     ws = _sync_ws(sdc_diff_ws_bytes(T, cap), dev)
     n = ctypes.c_uint64(0)
     idx = (ctypes.c_uint64 * max(cap, 1))()
@@ -478,6 +502,7 @@ def sdc_ring_compare(table, n, offset, stream=None):
     replayer r) of a contiguous int64 device table [n, 2, width] (synchronous)."""
     if table.dtype != torch.int64 or not table.is_contiguous() or table.numel() % (2 * n):
         raise ValueError("table must be a contiguous int64 [n, 2, width] device tensor")
+    _arg(table, "table", torch.int64, 0, table.device)
     width = table.numel() // (2 * n)
     ws = _sync_ws(sdc_ring_ws_bytes(n), table.device)
     flags = (ctypes.c_uint8 * n)()
@@ -504,6 +529,7 @@ def sdc_confirm_verdict(third, self_, orig, peer, stream=None):
     for v in vs:
         if v.dtype != torch.int64 or not v.is_contiguous() or v.numel() != width:
             raise ValueError("the four results must be contiguous int64 tensors of one length")
+        _arg(v, "a result", torch.int64, width, third.device)
     ws = _sync_ws(sdc_ring_ws_bytes(1), third.device)
     out = ctypes.c_int32(0)
     _check(_lib.sdc_confirm_verdict(*[ctypes.c_void_p(v.data_ptr()) for v in vs], width,
@@ -523,6 +549,9 @@ def sdc_sqnorm(plan, sq=None, total=None, flag=None, stream=None):
         total = torch.empty(1, dtype=torch.float64, device=dev)
     if flag is None:
         flag = torch.empty(1, dtype=torch.int32, device=dev)
+    _arg(sq, "sq", torch.float64, plan.n_tensors, dev)
+    _arg(total, "total", torch.float64, 1, dev)
+    _arg(flag, "flag", torch.int32, 1, dev)
     _check(_lib.sdc_sqnorm(ctypes.c_void_p(plan.buf.data_ptr()), ctypes.byref(plan.info),
                            ctypes.c_void_p(sq.data_ptr()), ctypes.c_void_p(total.data_ptr()),
                            ctypes.c_void_p(flag.data_ptr()), _stream_handle(stream, dev)),

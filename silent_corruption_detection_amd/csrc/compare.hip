@@ -434,7 +434,12 @@ extern "C" int32_t sdc_ring_localize(const uint8_t* h_mismatch, uint32_t n, uint
                                      uint8_t* h_culprit, uint8_t* h_ambiguous) {
   if (n == 0 || h_mismatch == nullptr || h_culprit == nullptr || h_ambiguous == nullptr)
     return SDC_ERR_INVALID;
-  std::vector<uint32_t> hits(n, 0);
+  std::vector<uint32_t> hits;
+  try {
+    hits.assign(n, 0u);
+  } catch (...) {
+    return SDC_ERR_RANGE;  // host allocation failed
+  }
   for (uint32_t r = 0; r < n; ++r) {
     if (!h_mismatch[r]) continue;
     hits[(uint32_t)(((uint64_t)r + offset) % n)]++;
@@ -488,6 +493,13 @@ extern "C" int32_t sdc_majority_compare(const sdc_row* d_table, uint32_t R, uint
     return SDC_ERR_INVALID;
   if ((uint64_t)R * T / R != T || (uint64_t)R * T >= (1ull << 58)) return SDC_ERR_RANGE;
   if (ws_bytes < maj_ws_bytes(R)) return SDC_ERR_WORKSPACE;
+  // host staging of the result and the flag bytes, allocated before anything is queued
+  thread_local std::vector<unsigned char> stage;
+  try {
+    stage.resize(sizeof(sdc_majority) + R);
+  } catch (...) {
+    return SDC_ERR_RANGE;  // host allocation failed
+  }
   hipStream_t s = as_stream(stream);
   unsigned char* base = reinterpret_cast<unsigned char*>(d_ws);
   MajWS* ws = reinterpret_cast<MajWS*>(base);
@@ -510,8 +522,6 @@ extern "C" int32_t sdc_majority_compare(const sdc_row* d_table, uint32_t R, uint
     if ((st = launch_status())) return st;
   }
   // one copy of the result and the flag bytes, then split on the host
-  thread_local std::vector<unsigned char> stage;
-  stage.resize(sizeof(sdc_majority) + R);
   if ((st = hip_status(hipMemcpyAsync(stage.data(), base + kMajOut, stage.size(),
                                       hipMemcpyDeviceToHost, s))))
     return st;
@@ -524,7 +534,7 @@ extern "C" int32_t sdc_majority_compare(const sdc_row* d_table, uint32_t R, uint
 extern "C" int32_t sdc_diff_ws_bytes(uint64_t T, uint64_t idx_cap, uint64_t* h_bytes) {
   if (h_bytes == nullptr) return SDC_ERR_INVALID;
   if (T >= (1ull << 58) || idx_cap >= (1ull << 58)) return SDC_ERR_RANGE;
-  *h_bytes = diff_layout(T, idx_cap).bytes;
+  *h_bytes = diff_layout(T, std::min(idx_cap, T)).bytes;  // at most T rows differ
   return SDC_OK;
 }
 
@@ -540,9 +550,17 @@ extern "C" int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, 
   }
   if (d_a == nullptr || d_b == nullptr || d_ws == nullptr) return SDC_ERR_INVALID;
   if (T >= (1ull << 58) || idx_cap >= (1ull << 58)) return SDC_ERR_RANGE;
-  const DiffLayout L = diff_layout(T, idx_cap);
+  const uint64_t cap = std::min(idx_cap, T);  // at most T rows differ
+  const DiffLayout L = diff_layout(T, cap);
   if (ws_bytes < L.bytes) return SDC_ERR_WORKSPACE;
   if (L.nb > kMaxGrid) return SDC_ERR_RANGE;
+  // host staging of the count and records, allocated before anything is queued
+  thread_local std::vector<unsigned char> stage;
+  try {
+    stage.resize(L.recs_off + cap * sizeof(DiffRec));
+  } catch (...) {
+    return SDC_ERR_RANGE;  // host allocation failed
+  }
   hipStream_t s = as_stream(stream);
   unsigned char* base = reinterpret_cast<unsigned char*>(d_ws);
   unsigned long long* n_diff = reinterpret_cast<unsigned long long*>(base);
@@ -551,7 +569,7 @@ extern "C" int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, 
   int32_t st;
   if (L.nb == 1) {
     hipLaunchKernelGGL(diff_fused, dim3(1), dim3(kBlock), 0, s, d_a, d_b, T, col_mask, n_diff, recs,
-                       hints, idx_cap);
+                       hints, cap);
     if ((st = launch_status())) return st;
   } else {
     unsigned long long* counts = reinterpret_cast<unsigned long long*>(base + L.counts_off);
@@ -562,13 +580,11 @@ extern "C" int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, 
     hipLaunchKernelGGL(diff_scan, dim3(1), dim3(kBlock), 0, s, counts, offsets, L.nb, n_diff);
     if ((st = launch_status())) return st;
     hipLaunchKernelGGL(diff_write, dim3((uint32_t)L.nb), dim3(kBlock), 0, s, d_a, d_b, T, col_mask,
-                       offsets, recs, hints, idx_cap);
+                       offsets, recs, hints, cap);
     if ((st = launch_status())) return st;
   }
   // The count and the first records in one copy; the rest only if there are more.
-  const uint64_t first = std::min(idx_cap, kDiffInline);
-  thread_local std::vector<unsigned char> stage;
-  stage.resize(L.recs_off + idx_cap * sizeof(DiffRec));
+  const uint64_t first = std::min(cap, kDiffInline);
   if ((st = hip_status(hipMemcpyAsync(stage.data(), base, L.recs_off + first * sizeof(DiffRec),
                                       hipMemcpyDeviceToHost, s))))
     return st;
@@ -576,7 +592,7 @@ extern "C" int32_t sdc_fingerprint_diff(const sdc_row* d_a, const sdc_row* d_b, 
   uint64_t n;
   std::memcpy(&n, stage.data(), 8);
   *h_n_diff = n;
-  const uint64_t m = std::min(n, idx_cap);
+  const uint64_t m = std::min(n, cap);
   if (m > first) {
     if ((st = hip_status(hipMemcpyAsync(stage.data() + L.recs_off + first * sizeof(DiffRec),
                                         base + L.recs_off + first * sizeof(DiffRec),

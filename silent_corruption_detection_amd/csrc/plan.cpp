@@ -66,7 +66,7 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
     const uint32_t es = element_size(t[k].dtype);
     if (es == 0) return SDC_ERR_DTYPE;
     if (!has_data(t[k])) continue;
-    if (t[k].numel >= (1ull << 62)) return SDC_ERR_RANGE;
+    if (t[k].numel >= (1ull << 62) / es) return SDC_ERR_RANGE;  // bytes < 2^62: no overflow below
     if (reinterpret_cast<uintptr_t>(t[k].ptr) % es != 0) return SDC_ERR_ALIGN;
     elems += t[k].numel;
     bytes += t[k].numel * es;
@@ -80,7 +80,8 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
       if (!has_data(t[k])) continue;
       const uint64_t ptr = reinterpret_cast<uintptr_t>(t[k].ptr);
       const uint32_t es = element_size(t[k].dtype);
-      for (int c = 0; c < kCand; ++c) cnt[c] += items_of(ptr, t[k].numel, es, kAutoMax >> c);
+      for (int c = 0; c < kCand; ++c)  // saturating: each term is below 2^62
+        cnt[c] = std::min<uint64_t>(cnt[c] + items_of(ptr, t[k].numel, es, kAutoMax >> c), 1ull << 62);
     }
     item_bytes = kAutoMin;
     for (int c = 0; c < kCand; ++c)
@@ -100,6 +101,7 @@ int32_t layout_plan(const sdc_tensor* t, uint64_t n, uint64_t item_bytes, Layout
     const uint32_t es = element_size(t[k].dtype);
     const uint64_t c = items_of(ptr, t[k].numel, es, item_bytes);
     items += c;
+    if (items > kMaxGrid) return SDC_ERR_RANGE;  // before the running sum could wrap
     const int wc = wave_class(ptr, t[k].numel, es, item_bytes);
     if (wc != kClassBlock) {
       small++;

@@ -115,7 +115,7 @@ int32_t tensor_shape(const sdc_tensor* t, uint64_t item_bytes, TensorShape* sh) 
   if ((t->flags & ~(uint32_t)SDC_FLAG_SIGNED) != 0) return SDC_ERR_INVALID;
   const uint32_t es = element_size(t->dtype);
   if (es == 0) return SDC_ERR_DTYPE;
-  if (t->numel >= (1ull << 62)) return SDC_ERR_RANGE;
+  if (t->numel >= (1ull << 62) / es) return SDC_ERR_RANGE;  // bytes < 2^62
   const uint64_t numel = t->ptr ? t->numel : 0u;
   const uint64_t ptr = reinterpret_cast<uintptr_t>(t->ptr);
   if (ptr % es != 0) return SDC_ERR_ALIGN;

@@ -103,6 +103,8 @@ def test_fingerprint_ws_bytes_is_the_automatic_plan_size():
     ((0x10000, 10, 0, 0), 24, -1),     # item size not a multiple of 16
     ((0x10000, 10, 0, 0), 8 << 20, -1),  # item size above 4 MiB
     ((0x10000, 1 << 62, 0, 0), 0, -7),  # too many elements
+    ((0x10000, 1 << 59, 3, 0), 0, -7),  # fp64: 2^62 bytes (below 2^62 elements)
+    ((0x10000, (1 << 60) - 1, 0, 0), 4 << 20, -7),  # fp32, just under 2^62 bytes: too many items
 ])
 def test_plan_validation_errors(desc, item_bytes, code):
     rc, _ = plan_bytes([desc], item_bytes)
@@ -112,9 +114,12 @@ def test_plan_validation_errors(desc, item_bytes, code):
 def test_workspace_sizing():
     import silent_corruption_detection_amd as sdc
     assert sdc.sdc_majority_ws_bytes(3, 100) > 0
-    # the workspace holds a 24-byte record (index + flip hint) per reported row
-    assert sdc.sdc_diff_ws_bytes(100, 1000) >= sdc.sdc_diff_ws_bytes(100, 0) + 24 * 1000 - 256
+    # the workspace holds a 24-byte record (index + flip hint) per reported row,
+    # and at most T rows can differ, so a cap above T counts as T
+    assert sdc.sdc_diff_ws_bytes(5000, 1000) >= sdc.sdc_diff_ws_bytes(5000, 0) + 24 * 1000 - 256
     assert sdc.sdc_diff_ws_bytes(100, 10) >= 16 + 24 * 10
+    assert sdc.sdc_diff_ws_bytes(100, 1000) == sdc.sdc_diff_ws_bytes(100, 100)
+    assert sdc.sdc_diff_ws_bytes(100, (1 << 58) - 1) == sdc.sdc_diff_ws_bytes(100, 100)
     with pytest.raises(sdc.SdcError):
         sdc.sdc_majority_ws_bytes(0, 10)
 
@@ -191,7 +196,8 @@ def test_tensor_automatic_item_size(desc):
 
 @pytest.mark.parametrize("desc,item_bytes,code", [
     ((0x10000, 10, 99, 0), 0, -2), ((0x10001, 10, 0, 0), 0, -3), ((0x10000, 10, 0, 2), 0, -1),
-    ((0x10000, 1 << 62, 0, 0), 0, -7), ((0x10000, 10, 0, 0), 24, -1),
+    ((0x10000, 1 << 62, 0, 0), 0, -7), ((0x10000, 1 << 59, 3, 0), 0, -7),
+    ((0x10000, 10, 0, 0), 24, -1),
     ((0x10000, 10, 0, 0), 8 << 20, -1)])
 def test_tensor_ws_bytes_errors(desc, item_bytes, code):
     assert tensor_ws_bytes(desc, item_bytes)[0] == code

@@ -327,6 +327,29 @@ def test_diff_matches_oracle():
                 assert got["hints"] == ref["hints"]
         got = sdc.sdc_fingerprint_diff(to_dev(a), to_dev(b), hints=False)
         assert got["indices"] == O.fingerprint_diff(a, b, O.COL_ALL, cap=T)["indices"]
+        if T <= 1025:  # an index cap far above T, through the C ABI: it counts as T
+            say(f"case diff T={T} huge cap")
+            got = diff_raw(to_dev(a), to_dev(b), T, (1 << 58) - 1)
+            ref = O.fingerprint_diff(a, b, O.COL_ALL, cap=T)
+            assert got == (0, ref["n_diff"], ref["indices"])
+
+
+def diff_raw(da, db, T, cap):
+    """sdc_fingerprint_diff through ctypes with an index array of T entries
+    (what the call may write: min(n_diff, cap) <= T)."""
+    import ctypes
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    ws_b = ctypes.c_uint64(0)
+    assert lib.sdc_diff_ws_bytes(ctypes.c_uint64(T), ctypes.c_uint64(cap), ctypes.byref(ws_b)) == 0
+    ws = torch.empty(ws_b.value, dtype=torch.uint8, device=DEV)
+    n = ctypes.c_uint64(0)
+    idx = (ctypes.c_uint64 * T)()
+    st = lib.sdc_fingerprint_diff(
+        ctypes.c_void_p(da.data_ptr()), ctypes.c_void_p(db.data_ptr()), ctypes.c_uint64(T),
+        ctypes.c_uint32(O.COL_ALL), ctypes.c_void_p(ws.data_ptr()), ctypes.c_uint64(ws.numel()),
+        ctypes.byref(n), idx, ctypes.c_uint64(cap), None,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    return st, n.value, [int(idx[i]) for i in range(min(n.value, T))]
 
 
 # ---------------------------------------------------------------------------
