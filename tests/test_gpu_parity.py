@@ -129,10 +129,15 @@ def test_launch_shapes_rows_counts_and_norms():
             iv[p] = v - (1 << (8 * es)) if v >= 1 << (8 * es - 1) else v
         tensors.append(t)
     tensors.append(random_bits(2 * 2_000_005, seed=77).view(torch.bfloat16))
+    # small tensors (wave items), a missing and an empty one in the same launches
+    tiny = random_bits(4 * 3000 + 16, seed=78)
+    tensors += [carve(tiny, 4, 1, torch.float32), None, carve(tiny, 2, 7, torch.bfloat16),
+                tiny[:0].view(torch.float16), carve(tiny, 6, 2000, torch.float16),
+                carve(tiny, 8, 100, torch.float32)]
     ref_rows = oracle_rows(tensors)
     ref_nf = oracle_nonfinite(tensors)
     ref_sq = oracle_sqnorms(tensors)
-    numels = [t.numel() for t in tensors]
+    numels = [0 if t is None else t.numel() for t in tensors]
     assert int(ref_nf[3]) > 5_000  # the random-bits tensor: about 2M / 256 NaN/Inf
     for ib, want in ((65536, "short"), (256 << 10, "deep"), (1 << 20, "wide"), (4 << 20, "wide")):
         plan = sdc.sdc_plan_build(tensors, item_bytes=ib)
