@@ -385,6 +385,33 @@ def test_all_types_sizes_offsets(dtype, signed):
         assert int(total.item()) == int(ref[:, 3].sum())
 
 
+@pytest.mark.parametrize("dtype", ALL_TYPES, ids=[str(t).split(".")[1] for t in ALL_TYPES])
+@pytest.mark.parametrize("signed", [False, True])
+def test_all_types_deep_and_wide_shapes(dtype, signed):
+    # the deep (96-512 KiB items) and wide (>= 512 KiB) launch shapes for every
+    # element type and widening mode: rows, NaN/Inf counts and squared norms
+    from _util import assert_sq_close, oracle_sqnorms
+    es = torch.empty(0, dtype=dtype).element_size()
+    n = 3_000_007
+    buf = random_bits(n * es + 16, seed=2000 + es)
+    tensors = [carve(buf, off, n, dtype) for off in range(0, 16, max(es, 4))]
+    ref = oracle_rows(tensors, flags=O.SIGNED if signed else 0)
+    ref_sq = oracle_sqnorms(tensors)
+    for ib, want in ((256 << 10, "deep"), (1 << 20, "wide"), (4 << 20, "wide")):
+        plan = sdc.sdc_plan_build(tensors, item_bytes=ib, signed=signed)
+        avg = plan.total_bytes // plan.n_items
+        assert ("wide" if avg >= 512 << 10 else "deep" if avg >= 96 << 10 else "short") == want
+        say(f"case types shape={want} dtype={dtype} signed={signed} item_bytes={ib}")
+        out = sdc.sdc_fingerprint_plan(plan)
+        counts, total = sdc.sdc_nonfinite(plan)
+        sq, _, _ = sdc.sdc_sqnorm(plan)
+        torch.cuda.synchronize()
+        assert_rows_equal(sdc.rows_numpy(out), ref)
+        assert counts.cpu().numpy().astype(np.uint64).tolist() == ref[:, 3].tolist()
+        assert int(total.item()) == int(ref[:, 3].sum())
+        assert_sq_close(sq.cpu().tolist(), ref_sq, [t.numel() for t in tensors])
+
+
 def test_all_types_item_sizes_and_mixed_lists():
     rng = np.random.default_rng(99)
     tensors = []
