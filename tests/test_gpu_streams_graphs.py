@@ -38,14 +38,23 @@ def mixed_list(seed):
     return out
 
 
-def test_two_streams_concurrently():
+# item sizes of the plans and single-tensor scans: automatic (short launch
+# shape for these lists), and 1 MiB (the wide shapes: one workgroup per CU
+# through a dynamic-LDS reservation, for the plans and the single tensors)
+ITEMS = [0, 1 << 20]
+
+
+@pytest.mark.parametrize("ib", ITEMS)
+def test_two_streams_concurrently(ib):
     a, b = mixed_list(1), mixed_list(2)
-    pa, pb = sdc.sdc_plan_build(a), sdc.sdc_plan_build(b)
+    pa, pb = sdc.sdc_plan_build(a, item_bytes=ib), sdc.sdc_plan_build(b, item_bytes=ib)
+    if ib:
+        assert pa.total_bytes // pa.n_items >= 512 << 10
     oa = torch.empty((len(a), 4), dtype=torch.int64, device=DEV)
     ob = torch.empty_like(oa)
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
-    say("case two streams")
+    say(f"case two streams item_bytes={ib}")
     for _ in range(5):
         with torch.cuda.stream(s1):
             sdc.sdc_fingerprint_plan(pa, oa)
@@ -56,24 +65,25 @@ def test_two_streams_concurrently():
     assert_rows_equal(sdc.rows_numpy(ob), oracle_rows(b))
     # single-tensor scans on both streams, each with its own reused workspace
     ta, tb = a[4], b[3]
-    wa = torch.empty(sdc.sdc_tensor_ws_bytes(ta), dtype=torch.uint8, device=DEV)
-    wb = torch.empty(sdc.sdc_tensor_ws_bytes(tb), dtype=torch.uint8, device=DEV)
+    wa = torch.empty(sdc.sdc_tensor_ws_bytes(ta, item_bytes=ib), dtype=torch.uint8, device=DEV)
+    wb = torch.empty(sdc.sdc_tensor_ws_bytes(tb, item_bytes=ib), dtype=torch.uint8, device=DEV)
     ra = torch.empty((1, 4), dtype=torch.int64, device=DEV)
     rb = torch.empty_like(ra)
     for _ in range(5):
         with torch.cuda.stream(s1):
-            sdc.sdc_fingerprint_tensor(ta, out=ra, ws=wa)
+            sdc.sdc_fingerprint_tensor(ta, out=ra, ws=wa, item_bytes=ib)
         with torch.cuda.stream(s2):
-            sdc.sdc_fingerprint_tensor(tb, out=rb, ws=wb)
+            sdc.sdc_fingerprint_tensor(tb, out=rb, ws=wb, item_bytes=ib)
     torch.cuda.synchronize()
     assert_rows_equal(sdc.rows_numpy(ra), oracle_rows([ta]))
     assert_rows_equal(sdc.rows_numpy(rb), oracle_rows([tb]))
 
 
-def test_graph_capture_and_replay():
+@pytest.mark.parametrize("ib", ITEMS)
+def test_graph_capture_and_replay(ib):
     ts = mixed_list(3)
     big = ts[4]
-    plan = sdc.sdc_plan_build(ts)
+    plan = sdc.sdc_plan_build(ts, item_bytes=ib)
     n = len(ts)
     rows = torch.empty((n, 4), dtype=torch.int64, device=DEV)
     counts = torch.empty(n, dtype=torch.int64, device=DEV)
@@ -81,7 +91,7 @@ def test_graph_capture_and_replay():
     sq = torch.empty(n, dtype=torch.float64, device=DEV)
     sq_total = torch.empty(1, dtype=torch.float64, device=DEV)
     flag = torch.empty(1, dtype=torch.int32, device=DEV)
-    ws = torch.empty(sdc.sdc_tensor_ws_bytes(big), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(sdc.sdc_tensor_ws_bytes(big, item_bytes=ib), dtype=torch.uint8, device=DEV)
     ref = sdc.sdc_fingerprint_tensor(big).clone()
     one = torch.empty((1, 4), dtype=torch.int64, device=DEV)
     mis = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -92,7 +102,7 @@ def test_graph_capture_and_replay():
         sdc.sdc_fingerprint_plan(plan, rows)
         sdc.sdc_nonfinite(plan, counts, total)
         sdc.sdc_sqnorm(plan, sq, sq_total, flag)
-        sdc.sdc_fingerprint_tensor(big, out=one, ref=ref, mismatch=mis, ws=ws)
+        sdc.sdc_fingerprint_tensor(big, out=one, ref=ref, mismatch=mis, ws=ws, item_bytes=ib)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -101,7 +111,7 @@ def test_graph_capture_and_replay():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    say("case graph capture")
+    say(f"case graph capture item_bytes={ib}")
     with torch.cuda.graph(g):
         work()
     torch.cuda.synchronize()
