@@ -268,14 +268,17 @@ constexpr uint64_t kCheckDeepItemBytes = 96ull << 10;
 // them), and one workgroup per CU.  The launch reserves kWideLdsBytes of
 // dynamic LDS that no kernel touches: a CU has 160 KiB, so a second
 // workgroup never fits.  HBM streams best with about 8-12 MiB of reads in
-// flight over the chip; the default shapes (2-4 workgroups per CU, pipelined
-// rounds) keep more than that outstanding and lose 4-5 % to it.  Measured on
-// the 141 GB Llama-70B bf16 list (1 MiB items, median of 10 scans, one box):
-// this shape 7.46 TB/s, two workgroups per CU with pipelined 8-vector rounds
-// (the shape used below the threshold) 7.13; 10 / 14 / 16 vectors per round
-// 7.40 / 7.39 / 7.41; pipelined rounds at one workgroup per CU 7.29.  With
-// 128 KiB items one workgroup per CU loses 25 % (each item's start-up
-// latency is then exposed), hence the threshold.
+// flight over the chip, issued by as few concurrent workgroups as can keep
+// that many in flight (each reads its own region): the default shapes (2-4
+// workgroups per CU, pipelined rounds) lose 4-5 % to it, and so do 2-4
+// workgroups per CU with the same reads in flight in shallower rounds.
+// Measured on the 141 GB Llama-70B bf16 list (1 MiB items, median of 10
+// scans, one box): this shape 7.46 TB/s, two workgroups per CU with pipelined
+// 8-vector rounds (the shape used below the threshold) 7.13; 10 / 14 / 16
+// vectors per round 7.40 / 7.39 / 7.41; pipelined rounds at one workgroup per
+// CU 7.29; 6 vectors at two workgroups per CU 7.12.  With 128 KiB items one
+// workgroup per CU loses 25 % (each item's start-up latency is then
+// exposed), hence the threshold.
 constexpr int kWideU = 12;
 constexpr uint64_t kWideItemBytes = 512ull << 10;
 constexpr uint32_t kWideLdsBytes = 96u << 10;
