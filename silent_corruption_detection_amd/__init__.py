@@ -343,10 +343,30 @@ def sdc_fingerprint_ws_bytes(tensors, signed=False):
     return nbytes.value
 
 
+def _one_descriptor(t, signed):
+    """One tensor (or None) -> (sdc_tensor struct, device, [tensor the
+    library reads]): _descriptors without the numpy table, which costs a few
+    microseconds per call that the single-tensor scan would pay every time."""
+    if t is None:
+        return _Tensor(0, 0, F32, 0), None, []
+    code = _TORCH_DTYPE.get(t.dtype)
+    if code is None:
+        raise TypeError(f"tensor 0: unsupported dtype {t.dtype}")
+    d = t.get_device()
+    if d < 0:
+        raise ValueError("tensor 0 is not on a GPU")
+    if not t.is_contiguous():
+        t = t.contiguous()
+    n = t.numel()
+    return (_Tensor(t.data_ptr() if n else 0, n, code, FLAG_SIGNED if signed else 0),
+            torch.device("cuda", d), [t])
+
+
 def sdc_tensor_ws_bytes(t, item_bytes=0, signed=False):
-    arr, _, _ = _descriptors([t], require_contiguous=False, signed=signed)
+    desc, _, _ = _one_descriptor(t, signed)
     b = ctypes.c_uint64(0)
-    _check(_lib.sdc_tensor_ws_bytes(arr, item_bytes, ctypes.byref(b)), "sdc_tensor_ws_bytes")
+    _check(_lib.sdc_tensor_ws_bytes(ctypes.byref(desc), item_bytes, ctypes.byref(b)),
+           "sdc_tensor_ws_bytes")
     return b.value
 
 
@@ -358,7 +378,8 @@ def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_AL
     one-element int32 device tensor the caller cleared).  `ws`: a uint8
     device workspace of at least sdc_tensor_ws_bytes bytes, reusable by calls
     on the same stream (they run in order); by default one is allocated."""
-    arr, dev, keep = _descriptors([t], require_contiguous=False, signed=signed)
+    desc, dev, keep = _one_descriptor(t, signed)
+    arr = ctypes.byref(desc)
     if dev is None:
         dev = torch.device("cuda")
     nb = ctypes.c_uint64(0)
