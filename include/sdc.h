@@ -35,6 +35,12 @@
  *     order fixed by the plan.
  *   - Functions are thread-safe.  Two scans that write the same output rows
  *     must not run concurrently.
+ *   - Launch shapes: scans of large items (list scans whose items average at
+ *     least 512 KiB, single-tensor scans of at least 128 MiB) run one
+ *     256-lane workgroup per CU; their launches reserve 96 KiB of dynamic LDS
+ *     per workgroup (untouched) to hold the CU to one, so work on other
+ *     streams shares those CUs only as far as LDS allows.  Results do not
+ *     depend on the shape.
  */
 #ifndef SDC_H
 #define SDC_H
