@@ -13,9 +13,11 @@ from the oracle, never from the HIP path:
           gives the flipped element and bit.
   c4      rows equal the oracle's for all 300,000 tensors; the named replicas
           are those the corruptions went to.
-  c5      (141 GB) rows of a sample of tensors equal the oracle's; a second
-          scan is identical to the first (diff empty); one seeded flip gives
-          exactly one differing tensor with the exact localisation.
+  c5      (141 GB) rows of a sample of tensors equal the oracle's, and so do
+          their squared norms (within the summation bound); no NaN/Inf is
+          counted and the norm check is clear; a second scan is identical to
+          the first (diff empty); one seeded flip gives exactly one differing
+          tensor with the exact localisation.
 """
 import gc
 
@@ -139,6 +141,16 @@ def test_c5_llama70b_bf16():
     say("case c5: oracle on a sample of tensors")
     assert_rows_equal(sdc.rows_numpy(out)[sample], oracle_rows([w.tensors[k] for k in sample]),
                       [w.names[k] for k in sample])
+    # the NaN/Inf-count and squared-norm scans on the same list (wide launch shape)
+    say("case c5: NaN/Inf counts and squared norms")
+    counts, total = sdc.sdc_nonfinite(plan)
+    sq, sq_total, flag = sdc.sdc_sqnorm(plan)
+    torch.cuda.synchronize()
+    assert int(total.item()) == 0 and int(counts.sum().item()) == 0
+    assert int(flag.item()) == 0
+    picked = [w.tensors[k] for k in sample]
+    assert_sq_close(sq.cpu().numpy()[sample].tolist(), oracle_sqnorms(picked),
+                    [t.numel() for t in picked])
     sdc.sdc_fingerprint_plan(plan, out)
     d = sdc.sdc_fingerprint_diff(first, out)
     assert d["n_diff"] == 0
