@@ -157,9 +157,18 @@ typedef struct {
   int32_t dir;    /* +1: bit is 0 in a and 1 in b; -1: 1 in a, 0 in b; 0: none */
 } sdc_flip_hint;
 
-/* ---- plans: a fixed tensor list scanned many times ------------------------ */
+/* ---- plans: a fixed tensor list scanned many times ------------------------
+ * [BLOG] "Compare by fingerprint" fingerprints a tensor list by looping over
+ * the tensors and, within each, over fixed-size chunks, adding each chunk's
+ * sums into the tensor's row.  A plan is that loop laid out once on the host:
+ * every tensor cut into work items (chunks of at most 4 MiB, each a
+ * contiguous element range of one tensor), which the scan kernels process in
+ * parallel; the chunks' sums combine exactly as in that loop (concatenation
+ * identity W(A||B) = W(A) + W(B) + |A| S(B)).  Parameter pointers do not
+ * change between training steps, so one plan serves every check. */
 
-/* Device bytes needed for the plan of h_tensors[0..n).  item_bytes is the work
+/* Device bytes needed for the plan of h_tensors[0..n) ([BLOG] "Compare by
+ * fingerprint": the per-tensor chunk loop).  item_bytes is the work
  * item size in bytes (a multiple of 16, at most 4 MiB); 0 selects it
  * automatically: the largest power of two from 1 MiB down to 64 KiB that
  * still splits the list into at least 49152 items (else 64 KiB).  The rows do
@@ -167,7 +176,8 @@ typedef struct {
 int32_t sdc_plan_bytes(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_bytes,
                        uint64_t* h_bytes);
 
-/* Packs the descriptors of h_tensors[0..n) into a work list and copies it into
+/* [BLOG] "Compare by fingerprint" (the per-tensor chunk loop, laid out once):
+ * packs the descriptors of h_tensors[0..n) into a work list and copies it into
  * d_plan (plan_bytes bytes of device memory owned by the caller).  The plan
  * also holds the scratch partial rows of tensors split over several work
  * items, so scans that use the same plan must not overlap in time.
@@ -180,7 +190,8 @@ int32_t sdc_plan_build(const sdc_tensor* h_tensors, uint64_t n, uint64_t item_by
                        void* d_plan, uint64_t plan_bytes, sdc_plan_info* h_info,
                        sdc_stream_t stream);
 
-/* Host-only form of sdc_plan_build for inspection and testing: writes the
+/* [BLOG] "Compare by fingerprint" (the per-tensor chunk loop, laid out once).
+ * Host-only form of sdc_plan_build for inspection and testing: writes the
  * plan's descriptor part (everything but the scratch partial rows, i.e. the
  * first plan_bytes bytes it needs, at most sdc_plan_bytes) to host memory
  * h_plan and fills h_info.  No HIP call.  Layout of the image: a 64-byte
@@ -222,12 +233,15 @@ int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info, uint64_t*
 int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, double* d_sq,
                    double* d_total, uint32_t* d_flag, sdc_stream_t stream);
 
-/* Device workspace bytes of sdc_fingerprint on this list (the plan's size
- * with the automatic item size: sdc_plan_bytes(h_tensors, n, 0)).  Host only;
+/* [BLOG] "Compare by fingerprint": device workspace bytes of sdc_fingerprint
+ * on this list (the plan's size with the automatic item size:
+ * sdc_plan_bytes(h_tensors, n, 0)).  Host only;
  * errors as sdc_plan_bytes. */
 int32_t sdc_fingerprint_ws_bytes(const sdc_tensor* h_tensors, uint64_t n, uint64_t* h_bytes);
 
-/* One-shot form of sdc_plan_build + sdc_fingerprint_plan: d_ws is a device
+/* [BLOG] "Compare by fingerprint" (rows of a tensor list), [AEGIS] xorsum, and
+ * [BLOG] "Check 1" (the NaN/Inf count): one-shot form of sdc_plan_build +
+ * sdc_fingerprint_plan; the rows are those of sdc_fingerprint_plan.  d_ws is a device
  * workspace of at least sdc_fingerprint_ws_bytes(h_tensors, n) bytes that
  * holds the plan.  The plan upload is synchronous; the scan is asynchronous
  * on stream.  The workspace must not be reused before the scan has completed. */
@@ -236,10 +250,25 @@ int32_t sdc_fingerprint(const sdc_tensor* h_tensors, uint64_t n, void* d_ws, uin
 
 /* ---- one tensor, no plan ------------------------------------------------- */
 
-/* Device workspace bytes for sdc_fingerprint_tensor on *h_tensor with the
- * same item_bytes (32 bytes per work item, at least 32).  Host only.  Errors
- * as sdc_fingerprint_tensor's argument checks. */
+/* [AEGIS] "core method" item 4 (the recompute check's scan): device
+ * workspace bytes for sdc_fingerprint_tensor on *h_tensor with the same
+ * item_bytes: 32 bytes per work item, at least 32.  With the automatic item
+ * size the split of tensors of 128 MiB and more depends on the device's
+ * compute-unit count; the size returned then holds on every gfx950 device
+ * (at most 8 KiB more than one device needs).  Host only (no HIP call).
+ * Errors as sdc_fingerprint_tensor's argument checks. */
 int32_t sdc_tensor_ws_bytes(const sdc_tensor* h_tensor, uint64_t item_bytes, uint64_t* h_bytes);
+
+/* Host-only view of the split sdc_fingerprint_tensor makes of *h_tensor on a
+ * device with cu_count compute units (for inspection and testing; no HIP
+ * call): *h_n_items work items of *h_item_bytes bytes each (the first may
+ * also hold a misaligned head, the last may be shorter).  With item_bytes 0
+ * (automatic), tensors of at least 128 MiB take a multiple of
+ * min(cu_count, 256) items of at most 4 MiB (one per CU per pass); smaller
+ * ones about 1024 items of 64 KiB to 1 MiB.  Errors: SDC_ERR_INVALID
+ * (NULL outputs, cu_count 0), else as sdc_fingerprint_tensor's checks. */
+int32_t sdc_tensor_split_host(const sdc_tensor* h_tensor, uint64_t item_bytes, uint32_t cu_count,
+                              uint64_t* h_n_items, uint64_t* h_item_bytes);
 
 /* [AEGIS] "core method" item 4: fingerprints of an original result and of its
  * deterministic recomputation, compared bit for bit; any difference is a
@@ -333,14 +362,16 @@ int32_t sdc_ring_compare(const uint64_t* d_table, uint32_t n, uint64_t width, ui
 int32_t sdc_ring_localize(const uint8_t* h_mismatch, uint32_t n, uint32_t offset,
                           uint8_t* h_culprit, uint8_t* h_ambiguous);
 
-/* Confirmation of an ambiguous pair: a third GPU (on another node) and the
- * target replay the target's work once more.  d_third, d_self: those two
- * replays; d_orig: the target's original own result; d_peer: the replayer's
- * replay; all `width` words of device memory.  Verdict: the replayer computed
- * wrong if the third GPU agrees with the original; otherwise, if it agrees
- * with the replayer, the target is the suspect -- persistent when the target
- * reproduced its original, transient when its retry agrees with the third
- * GPU, else unclear; if the third GPU agrees with neither, unattributable.
+/* Confirmation of an ambiguous pair ("Check 2", the case where only one of
+ * a rank's two comparisons mismatches): a witness GPU on a third node and the
+ * target itself replay the target's work once more.  d_witness, d_retry:
+ * those two replays; d_original: the target's first own result; d_replay:
+ * the replayer's replay of it; all `width` words of device memory.  Verdict,
+ * per the verdict rows of [BLOG] "Decide what the alarm means": the replayer
+ * computed wrong if the witness reproduces the original; otherwise, if the
+ * witness sides with the replayer, the target was wrong -- persistent when
+ * its retry reproduced its original, transient when its retry agrees with the
+ * witness, else unclear; if the witness agrees with neither, unattributable.
  * d_ws: sdc_ring_ws_bytes(1) bytes.  SYNCHRONOUS. */
 enum {
   SDC_VERDICT_REPLAYER_WRONG = 1, /* suspect: the replayer */
@@ -349,8 +380,8 @@ enum {
   SDC_VERDICT_UNCLEAR = 4,        /* suspect: the target   */
   SDC_VERDICT_UNATTRIBUTABLE = 5  /* no suspect            */
 };
-int32_t sdc_confirm_verdict(const uint64_t* d_third, const uint64_t* d_self,
-                            const uint64_t* d_orig, const uint64_t* d_peer, uint64_t width,
+int32_t sdc_confirm_verdict(const uint64_t* d_witness, const uint64_t* d_retry,
+                            const uint64_t* d_original, const uint64_t* d_replay, uint64_t width,
                             void* d_ws, uint64_t ws_bytes, int32_t* h_verdict,
                             sdc_stream_t stream);
 
@@ -376,13 +407,14 @@ int32_t sdc_read_sum(const void* d_buf, uint64_t bytes, void* d_ws, uint64_t ws_
 
 /* ---- misc ------------------------------------------------------------------ */
 
-/* Static text for a status code. */
+/* Static text for a status code (not from the pages). */
 const char* sdc_status_string(int32_t status);
 
-/* The hipError_t of the last failed HIP call on this thread (0 if none). */
+/* The hipError_t of the last failed HIP call on this thread (0 if none; not
+ * from the pages). */
 int32_t sdc_last_hip_error(void);
 
-/* SDC_ABI_VERSION of the library. */
+/* SDC_ABI_VERSION of the library (not from the pages). */
 uint32_t sdc_abi_version(void);
 
 #ifdef __cplusplus

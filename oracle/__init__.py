@@ -220,9 +220,12 @@ def ring_localize(mismatch, n, offset):
     return cul, amb
 
 
-def confirm_verdict(third, self_, orig, peer):
+def confirm_verdict(witness, retry, original, replay):
+    """Verdict code of a confirmation (see VERDICTS) from the witness GPU's
+    replay, the target's retry, the target's original result and the
+    replayer's replay."""
     arrs = [np.ascontiguousarray(np.asarray(a, dtype=np.uint64).reshape(-1))
-            for a in (third, self_, orig, peer)]
+            for a in (witness, retry, original, replay)]
     width = arrs[0].size
     v = ctypes.c_int32(0)
     _check(lib().oracle_confirm_verdict(*[a.ctypes.data if width else None for a in arrs], width,

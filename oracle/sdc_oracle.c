@@ -292,24 +292,43 @@ int oracle_ring_localize(const uint8_t* mismatch, uint32_t n, uint32_t offset, u
   return ORACLE_OK;
 }
 
-/* "Check 2", confirmation: if the third GPU agrees with the target's original
- * result, the replayer computed wrong; if it agrees with the replayer's
- * replay, the target is the suspect -- persistent when the target reproduces
- * its original, transient when its retry matches the third GPU, otherwise
- * unclear; if the third GPU agrees with neither, no one can be named. */
-int oracle_confirm_verdict(const uint64_t* third, const uint64_t* self, const uint64_t* orig,
-                           const uint64_t* peer, uint64_t width, int32_t* verdict) {
-  if (verdict == NULL || (width > 0 && (third == NULL || self == NULL || orig == NULL || peer == NULL)))
+/* "Check 2", confirmation, from the section's "Only one mismatches" case and
+ * the verdict rows of "Decide what the alarm means".  Two GPUs replay the
+ * target's work once more: a witness on a third node and the target itself
+ * (its retry).  Four equalities decide: witness == original (the target's own
+ * first result), witness == replay (the replayer's replay of that work),
+ * retry == original, retry == witness.
+ *   - The witness reproduces the original: the target was right, so the
+ *     replaying GPU was wrong ("replayer computed wrong").
+ *   - The witness sides with the replayer (and not with the original): the
+ *     target was wrong.  It reproduced its own wrong answer: "persistent";
+ *     its retry came out right, agreeing with the witness: "transient";
+ *     otherwise the three results do not line up: "unclear".
+ *   - The witness agrees with neither: nobody can be named ("unattributable").
+ * Indexed by the four equalities as bits (1: witness == original, 2: witness
+ * == replay, 4: retry == original, 8: retry == witness).  Where the witness
+ * equals both, the original equals the replay, and the pair did not mismatch;
+ * the first rule then still applies. */
+static const int32_t kVerdictOf[16] = {
+    /* 0b0000 */ ORACLE_VERDICT_UNATTRIBUTABLE, /* 0b0001 */ ORACLE_VERDICT_REPLAYER_WRONG,
+    /* 0b0010 */ ORACLE_VERDICT_UNCLEAR,        /* 0b0011 */ ORACLE_VERDICT_REPLAYER_WRONG,
+    /* 0b0100 */ ORACLE_VERDICT_UNATTRIBUTABLE, /* 0b0101 */ ORACLE_VERDICT_REPLAYER_WRONG,
+    /* 0b0110 */ ORACLE_VERDICT_PERSISTENT,     /* 0b0111 */ ORACLE_VERDICT_REPLAYER_WRONG,
+    /* 0b1000 */ ORACLE_VERDICT_UNATTRIBUTABLE, /* 0b1001 */ ORACLE_VERDICT_REPLAYER_WRONG,
+    /* 0b1010 */ ORACLE_VERDICT_TRANSIENT,      /* 0b1011 */ ORACLE_VERDICT_REPLAYER_WRONG,
+    /* 0b1100 */ ORACLE_VERDICT_UNATTRIBUTABLE, /* 0b1101 */ ORACLE_VERDICT_REPLAYER_WRONG,
+    /* 0b1110 */ ORACLE_VERDICT_PERSISTENT,     /* 0b1111 */ ORACLE_VERDICT_REPLAYER_WRONG};
+
+int oracle_confirm_verdict(const uint64_t* witness, const uint64_t* retry, const uint64_t* original,
+                           const uint64_t* replay, uint64_t width, int32_t* verdict) {
+  if (verdict == NULL ||
+      (width > 0 && (witness == NULL || retry == NULL || original == NULL || replay == NULL)))
     return ORACLE_EINVAL;
-  if (words_equal(third, orig, width)) {
-    *verdict = ORACLE_VERDICT_REPLAYER_WRONG;
-  } else if (words_equal(third, peer, width)) {
-    if (words_equal(self, orig, width)) *verdict = ORACLE_VERDICT_PERSISTENT;
-    else if (words_equal(self, third, width)) *verdict = ORACLE_VERDICT_TRANSIENT;
-    else *verdict = ORACLE_VERDICT_UNCLEAR;
-  } else {
-    *verdict = ORACLE_VERDICT_UNATTRIBUTABLE;
-  }
+  unsigned idx = (unsigned)words_equal(witness, original, width) |
+                 (unsigned)words_equal(witness, replay, width) << 1 |
+                 (unsigned)words_equal(retry, original, width) << 2 |
+                 (unsigned)words_equal(retry, witness, width) << 3;
+  *verdict = kVerdictOf[idx];
   return ORACLE_OK;
 }
 

@@ -155,9 +155,10 @@ int oracle_ring_pairs(const uint64_t* table, uint32_t n, uint64_t width, uint32_
 int oracle_ring_localize(const uint8_t* mismatch, uint32_t n, uint32_t offset, uint8_t* culprit,
                          uint8_t* ambiguous);
 
-/* Verdict of a confirmation: a third GPU and the target replay the target's
- * work again.  third/self: those replays; orig: the target's original own
- * result; peer: the replayer's replay.  All width words long. */
+/* Verdict of a confirmation: a witness GPU on a third node and the target
+ * itself (its retry) replay the target's work again.  original: the target's
+ * first own result; replay: the replayer's replay of it.  All width words
+ * long. */
 enum {
   ORACLE_VERDICT_REPLAYER_WRONG = 1, /* suspect: the replayer */
   ORACLE_VERDICT_PERSISTENT = 2,     /* suspect: the target   */
@@ -165,8 +166,8 @@ enum {
   ORACLE_VERDICT_UNCLEAR = 4,        /* suspect: the target   */
   ORACLE_VERDICT_UNATTRIBUTABLE = 5  /* no suspect            */
 };
-int oracle_confirm_verdict(const uint64_t* third, const uint64_t* self, const uint64_t* orig,
-                           const uint64_t* peer, uint64_t width, int32_t* verdict);
+int oracle_confirm_verdict(const uint64_t* witness, const uint64_t* retry, const uint64_t* original,
+                           const uint64_t* replay, uint64_t width, int32_t* verdict);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ __all__ = [
     "sdc_diff_ws_bytes", "sdc_fingerprint_diff", "sdc_status_string", "sdc_last_hip_error",
     "sdc_abi_version", "rows_numpy", "LIB_PATH", "sdc_ring_ws_bytes", "sdc_ring_compare",
     "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS", "sdc_sqnorm",
-    "sdc_tensor_ws_bytes", "sdc_fingerprint_tensor", "sdc_read_sum_ws_bytes", "sdc_read_sum",
+    "sdc_tensor_ws_bytes", "sdc_tensor_split_host", "sdc_fingerprint_tensor",
+    "sdc_read_sum_ws_bytes", "sdc_read_sum",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
@@ -85,6 +86,7 @@ def _load():
         "sdc_plan_pack_host": [P, U64, U64, P, U64, P],
         "sdc_sqnorm": [P, P, P, P, P, P],
         "sdc_tensor_ws_bytes": [P, U64, P],
+        "sdc_tensor_split_host": [P, U64, U32, P, P],
         "sdc_fingerprint_tensor": [P, U64, P, U64, P, U32, P, P, P],
         "sdc_ring_ws_bytes": [U32, P],
         "sdc_ring_compare": [P, U32, U64, U32, P, U64, P, P],
@@ -159,6 +161,25 @@ def _stream_handle(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _scan_stream(stream, device, made):
+    """The stream a call's library work goes on, ordered after what this call
+    made on the current stream.  `made`: tensors the binding itself wrote or
+    allocated on the current stream (contiguous copies of strided inputs, a
+    workspace, the output).  When the call's stream is another one, it first
+    waits for the current stream, so the copies are complete before the
+    library reads them and memory the allocator handed out is free on it; the
+    tensors are then marked as used on that stream, so the allocator keeps
+    them until its work has run."""
+    cur = torch.cuda.current_stream(device)
+    if stream is None or stream == cur:
+        return cur
+    stream.wait_stream(cur)
+    if not torch.cuda.is_current_stream_capturing():
+        for t in made:
+            t.record_stream(stream)
+    return stream
 
 
 def _same_device(a, b):
@@ -321,15 +342,13 @@ def sdc_fingerprint(tensors, out=None, stream=None, signed=False):
     _check(_lib.sdc_fingerprint_ws_bytes(arr, len(tensors), ctypes.byref(nbytes)),
            "sdc_fingerprint_ws_bytes")
     ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=dev)
+    made_out = out is None
     out = _rows_out(out, len(tensors), dev)
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    copies = [t for t, orig in zip(keep, (x for x in tensors if x is not None)) if t is not orig]
+    s = _scan_stream(stream, dev, [ws] + copies + ([out] if made_out else []))
     _check(_lib.sdc_fingerprint(arr, len(tensors), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream)),
            "sdc_fingerprint")
-    # keep the workspace and any contiguous copies alive until the scan ran
-    ws.record_stream(s)
-    for t in keep:
-        t.record_stream(s)
     return out
 
 
@@ -386,8 +405,13 @@ def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_AL
     _check(_lib.sdc_tensor_ws_bytes(arr, item_bytes, ctypes.byref(nb)), "sdc_tensor_ws_bytes")
     if ws is not None:
         _arg(ws, "ws", torch.uint8, 0, dev)
+    made = [x for x in keep if x is not t]  # a contiguous copy of a strided input
     if ws is None or ws.numel() < nb.value:
         ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+        made.append(ws)
+    if out is None:
+        out = _rows_out(None, 1, dev)
+        made.append(out)
     out = _rows_out(out, 1, dev)
     ref_p = mis_p = None
     if ref is not None:
@@ -396,18 +420,22 @@ def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_AL
             raise ValueError("a compare needs a one-element int32 mismatch counter")
         _arg(mismatch, "mismatch", torch.int32, 1, dev)
         ref_p, mis_p = ref.data_ptr(), mismatch.data_ptr()
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    s = _scan_stream(stream, dev, made)
     _check(_lib.sdc_fingerprint_tensor(arr, item_bytes, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                        ctypes.c_void_p(ref_p), col_mask,
                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(mis_p),
                                        ctypes.c_void_p(s.cuda_stream)), "sdc_fingerprint_tensor")
-    if not torch.cuda.is_current_stream_capturing():
-        # keep the workspace and any contiguous copy alive until the scan ran
-        # (under graph capture they belong to the graph's memory pool instead)
-        ws.record_stream(s)
-        for x in keep:
-            x.record_stream(s)
     return out
+
+
+def sdc_tensor_split_host(t, cu_count, item_bytes=0, signed=False):
+    """(work items, bytes per item) of sdc_fingerprint_tensor's split of t on a
+    device with cu_count compute units (host only)."""
+    desc, _, _ = _one_descriptor(t, signed)
+    n, ib = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check(_lib.sdc_tensor_split_host(ctypes.byref(desc), item_bytes, cu_count, ctypes.byref(n),
+                                      ctypes.byref(ib)), "sdc_tensor_split_host")
+    return n.value, ib.value
 
 
 def sdc_read_sum_ws_bytes(nbytes):
@@ -543,19 +571,21 @@ def sdc_ring_localize(mismatch, n, offset):
             np.frombuffer(bytes(amb), dtype=np.uint8).copy())
 
 
-def sdc_confirm_verdict(third, self_, orig, peer, stream=None):
-    """Verdict code (see VERDICTS) of a confirmation from four int64 device vectors."""
-    vs = [third, self_, orig, peer]
-    width = third.numel()
+def sdc_confirm_verdict(witness, retry, original, replay, stream=None):
+    """Verdict code (see VERDICTS) of a confirmation from four int64 device
+    vectors: the witness GPU's replay, the target's retry, the target's
+    original result and the replayer's replay."""
+    vs = [witness, retry, original, replay]
+    width = witness.numel()
     for v in vs:
         if v.dtype != torch.int64 or not v.is_contiguous() or v.numel() != width:
             raise ValueError("the four results must be contiguous int64 tensors of one length")
-        _arg(v, "a result", torch.int64, width, third.device)
-    ws = _sync_ws(sdc_ring_ws_bytes(1), third.device)
+        _arg(v, "a result", torch.int64, width, witness.device)
+    ws = _sync_ws(sdc_ring_ws_bytes(1), witness.device)
     out = ctypes.c_int32(0)
     _check(_lib.sdc_confirm_verdict(*[ctypes.c_void_p(v.data_ptr()) for v in vs], width,
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.byref(out),
-                                    _stream_handle(stream, third.device)), "sdc_confirm_verdict")
+                                    _stream_handle(stream, witness.device)), "sdc_confirm_verdict")
     return out.value
 
 

@@ -384,15 +384,15 @@ __global__ void __launch_bounds__(kBlock) ring_compare_kernel(const uint64_t* __
   if (threadIdx.x == 0) flags[r] = (uint8_t)(d != 0);
 }
 
-// Equality of four vector pairs (third, orig), (third, peer), (self, orig),
-// (self, third): one workgroup each.
-__global__ void __launch_bounds__(kBlock) confirm_kernel(const uint64_t* __restrict__ third,
-                                                         const uint64_t* __restrict__ self,
-                                                         const uint64_t* __restrict__ orig,
-                                                         const uint64_t* __restrict__ peer,
+// Equality of four vector pairs, one workgroup each: (witness, original),
+// (witness, replay), (retry, original), (retry, witness).
+__global__ void __launch_bounds__(kBlock) confirm_kernel(const uint64_t* __restrict__ witness,
+                                                         const uint64_t* __restrict__ retry,
+                                                         const uint64_t* __restrict__ original,
+                                                         const uint64_t* __restrict__ replay,
                                                          uint64_t width, uint8_t* eq) {
-  const uint64_t* a = blockIdx.x < 2 ? third : self;
-  const uint64_t* b = blockIdx.x == 0 ? orig : blockIdx.x == 1 ? peer : blockIdx.x == 2 ? orig : third;
+  const uint64_t* a = blockIdx.x < 2 ? witness : retry;
+  const uint64_t* b = (blockIdx.x & 1u) == 0 ? original : blockIdx.x == 1 ? replay : witness;
   uint32_t d = 0;
   for (uint64_t i = threadIdx.x; i < width; i += kBlock) d |= (a[i] != b[i]);
   d = block_or(d);
@@ -453,28 +453,39 @@ extern "C" int32_t sdc_ring_localize(const uint8_t* h_mismatch, uint32_t n, uint
   return SDC_OK;
 }
 
-extern "C" int32_t sdc_confirm_verdict(const uint64_t* d_third, const uint64_t* d_self,
-                                       const uint64_t* d_orig, const uint64_t* d_peer,
+extern "C" int32_t sdc_confirm_verdict(const uint64_t* d_witness, const uint64_t* d_retry,
+                                       const uint64_t* d_original, const uint64_t* d_replay,
                                        uint64_t width, void* d_ws, uint64_t ws_bytes,
                                        int32_t* h_verdict, sdc_stream_t stream) {
   if (h_verdict == nullptr || d_ws == nullptr ||
-      (width > 0 && (!d_third || !d_self || !d_orig || !d_peer)))
+      (width > 0 && (!d_witness || !d_retry || !d_original || !d_replay)))
     return SDC_ERR_INVALID;
   if (ws_bytes < 16) return SDC_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   uint8_t* eq_d = reinterpret_cast<uint8_t*>(d_ws);
-  hipLaunchKernelGGL(confirm_kernel, dim3(4), dim3(kBlock), 0, s, d_third, d_self, d_orig, d_peer,
-                     width, eq_d);
+  hipLaunchKernelGGL(confirm_kernel, dim3(4), dim3(kBlock), 0, s, d_witness, d_retry, d_original,
+                     d_replay, width, eq_d);
   int32_t st = launch_status();
   if (st) return st;
   uint8_t eq[4];
   if ((st = hip_status(hipMemcpyAsync(eq, eq_d, 4, hipMemcpyDeviceToHost, s)))) return st;
   if ((st = hip_status(hipStreamSynchronize(s)))) return st;
-  // eq: [third == orig, third == peer, self == orig, self == third]
-  if (eq[0]) *h_verdict = SDC_VERDICT_REPLAYER_WRONG;
-  else if (eq[1]) *h_verdict = eq[2] ? SDC_VERDICT_PERSISTENT
-                             : eq[3] ? SDC_VERDICT_TRANSIENT : SDC_VERDICT_UNCLEAR;
-  else *h_verdict = SDC_VERDICT_UNATTRIBUTABLE;
+  const bool witness_is_original = eq[0], witness_is_replay = eq[1];
+  const bool retry_is_original = eq[2], retry_is_witness = eq[3];
+  // The verdict rows of [BLOG] "Decide what the alarm means", as conditions on
+  // the four equalities.  The target was wrong when the witness sides with
+  // the replayer (and not with the original).
+  const bool target_wrong = witness_is_replay && !witness_is_original;
+  if (target_wrong && retry_is_original)
+    *h_verdict = SDC_VERDICT_PERSISTENT;  // reproduced its own wrong answer
+  else if (target_wrong && retry_is_witness)
+    *h_verdict = SDC_VERDICT_TRANSIENT;  // the retry came out right, as the witness
+  else if (witness_is_original)
+    *h_verdict = SDC_VERDICT_REPLAYER_WRONG;  // the witness reproduced the original
+  else if (target_wrong)
+    *h_verdict = SDC_VERDICT_UNCLEAR;  // the three do not line up
+  else
+    *h_verdict = SDC_VERDICT_UNATTRIBUTABLE;  // the witness agrees with neither side
   return SDC_OK;
 }
 

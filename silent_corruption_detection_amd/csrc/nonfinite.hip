@@ -51,8 +51,9 @@ template <int U, bool PIPE>
 __global__ void __launch_bounds__(kBlock) nonfinite_kernel(const PlanItem* __restrict__ items,
                                                            sdc_row* __restrict__ partials,
                                                            uint64_t* __restrict__ counts,
-                                                           uint64_t* __restrict__ total) {
-  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
+                                                           uint64_t* __restrict__ total,
+                                                           uint32_t xcds) {
+  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x, xcds)];
   uint32_t c = 0;
   dispatch_type(it.dtype_flags & ~kItemSigned,
                 [&](auto ty) { c = nonfinite_item<typename Unsigned<decltype(ty)>::type, U, PIPE>(it); });
@@ -151,19 +152,21 @@ extern "C" int32_t sdc_nonfinite(const void* d_plan, const sdc_plan_info* h_info
     if ((st = launch_status())) return st;
   }
   if (n_block) {
+    DeviceShape dev;
+    if ((st = current_device_shape(&dev))) return st;
     const dim3 grid((uint32_t)n_block), block(kBlock);
     switch (item_shape(h_info->total_bytes, h_info->n_items, kCheckDeepItemBytes)) {
       case kShapeWide:
         hipLaunchKernelGGL((nonfinite_kernel<kWideU, false>), grid, block, kWideLdsBytes, s, v.items,
-                           v.partials, d_counts, d_total);
+                           v.partials, d_counts, d_total, dev.xcds);
         break;
       case kShapeDeep:
         hipLaunchKernelGGL((nonfinite_kernel<kCheckDeepU, true>), grid, block, 0, s, v.items,
-                           v.partials, d_counts, d_total);
+                           v.partials, d_counts, d_total, dev.xcds);
         break;
       default:
         hipLaunchKernelGGL((nonfinite_kernel<kCheckU, true>), grid, block, 0, s, v.items, v.partials,
-                           d_counts, d_total);
+                           d_counts, d_total, dev.xcds);
     }
     if ((st = launch_status())) return st;
   }

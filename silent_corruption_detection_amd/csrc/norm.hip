@@ -138,8 +138,9 @@ __device__ __forceinline__ double sq_item(const PlanItem& it) {
 template <int U, bool PIPE>
 __global__ void __launch_bounds__(kBlock) sqnorm_kernel(const PlanItem* __restrict__ items,
                                                         sdc_row* __restrict__ partials,
-                                                        double* __restrict__ sq) {
-  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
+                                                        double* __restrict__ sq,
+                                                        uint32_t xcds) {
+  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x, xcds)];
   double acc = 0.0;
   dispatch_dtype(it.dtype_flags, [&](auto dt) { acc = sq_item<decltype(dt), U, PIPE>(it); });
   acc = block_sum_d(acc);
@@ -254,19 +255,21 @@ extern "C" int32_t sdc_sqnorm(const void* d_plan, const sdc_plan_info* h_info, d
     if ((st = launch_status())) return st;
   }
   if (n_block) {
+    DeviceShape dev;
+    if ((st = current_device_shape(&dev))) return st;
     const dim3 grid((uint32_t)n_block), block(kBlock);
     switch (item_shape(h_info->total_bytes, h_info->n_items, kCheckDeepItemBytes)) {
       case kShapeWide:
         hipLaunchKernelGGL((sqnorm_kernel<kWideU, false>), grid, block, kWideLdsBytes, s, v.items,
-                           v.partials, d_sq);
+                           v.partials, d_sq, dev.xcds);
         break;
       case kShapeDeep:
         hipLaunchKernelGGL((sqnorm_kernel<kCheckDeepU, true>), grid, block, 0, s, v.items, v.partials,
-                           d_sq);
+                           d_sq, dev.xcds);
         break;
       default:
         hipLaunchKernelGGL((sqnorm_kernel<kCheckU, true>), grid, block, 0, s, v.items, v.partials,
-                           d_sq);
+                           d_sq, dev.xcds);
     }
     if ((st = launch_status())) return st;
   }

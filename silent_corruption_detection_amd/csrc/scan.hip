@@ -49,8 +49,9 @@ namespace {
 template <class Cfg>
 __global__ void __launch_bounds__(kBlock) fingerprint_kernel(const PlanItem* __restrict__ items,
                                                              sdc_row* __restrict__ partials,
-                                                             sdc_row* __restrict__ out) {
-  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x)];
+                                                             sdc_row* __restrict__ out,
+                                                             uint32_t xcds) {
+  const PlanItem it = items[xcd_item(blockIdx.x, gridDim.x, xcds)];
   Lane ln;
   dispatch_type(it.dtype_flags, [&](auto ty) { scan_item<decltype(ty), Cfg>(it, ln); });
   if (threadIdx.x != 0) return;
@@ -112,18 +113,21 @@ int32_t launch_scan(const void* d_plan, const sdc_plan_info* h, sdc_row* out, hi
     if ((st = launch_status())) return st;
   }
   if (n_block) {
+    DeviceShape dev;
+    if ((st = current_device_shape(&dev))) return st;
     const dim3 grid((uint32_t)n_block), block(kBlock);
     switch (item_shape(h->total_bytes, h->n_items, kDeepItemBytes)) {
       case kShapeWide:
         hipLaunchKernelGGL(fingerprint_kernel<WideBody>, grid, block, kWideLdsBytes, s, v.items,
-                           v.partials, out);
+                           v.partials, out, dev.xcds);
         break;
       case kShapeDeep:
-        hipLaunchKernelGGL(fingerprint_kernel<DeepBody>, grid, block, 0, s, v.items, v.partials, out);
+        hipLaunchKernelGGL(fingerprint_kernel<DeepBody>, grid, block, 0, s, v.items, v.partials, out,
+                           dev.xcds);
         break;
       default:
         hipLaunchKernelGGL(fingerprint_kernel<DefaultBody>, grid, block, 0, s, v.items, v.partials,
-                           out);
+                           out, dev.xcds);
     }
     if ((st = launch_status())) return st;
   }

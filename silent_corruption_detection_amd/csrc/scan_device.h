@@ -382,24 +382,26 @@ __device__ __forceinline__ uint64_t load_elem(const unsigned char* p) {
   return *reinterpret_cast<const uint64_t*>(p);
 }
 
-// Item of workgroup b among the n workgroup items of a launch.  Workgroups go
-// to the 8 XCDs round-robin (b to XCD b % 8); within each window of
-// 8 * kXcdRun items, XCD k takes the kXcdRun adjacent items k*kXcdRun ..
-// (k+1)*kXcdRun - 1, so each XCD reads runs of neighbouring items while all
-// XCDs advance through the list together.  Items past the last whole window
-// keep their order.  A bijection on [0, n).  Measured against items in
-// workgroup order on plan scans: lists of 128 KiB items 1.1-1.9 % faster,
-// lists of small tensors 1 %, 1 MiB items unchanged; giving each XCD one
-// contiguous eighth of the list instead is 2-3 % faster on the first and
-// 5-7 % slower on a 141 GB list of 1 MiB items.  (The single-tensor scan keeps
-// workgroup order: its 512 KiB items measured 5 % slower with this mapping.)
-constexpr uint32_t kXcds = 8, kXcdRun = 16;
+// Item of workgroup b among the n workgroup items of a launch on a device
+// with `xcds` XCDs.  Workgroups go to the XCDs round-robin (b to XCD
+// b % xcds); within each window of xcds * kXcdRun items, XCD k takes the
+// kXcdRun adjacent items k*kXcdRun .. (k+1)*kXcdRun - 1, so each XCD reads
+// runs of neighbouring items while all XCDs advance through the list
+// together.  Items past the last whole window keep their order, and with one
+// XCD the map is the identity.  A bijection on [0, n).  Measured on the full
+// MI355X (8 XCDs) against items in workgroup order on plan scans: lists of
+// 128 KiB items 1.1-1.9 % faster, lists of small tensors 1 %, 1 MiB items
+// unchanged; giving each XCD one contiguous eighth of the list instead is
+// 2-3 % faster on the first and 5-7 % slower on a 141 GB list of 1 MiB
+// items.  (The single-tensor scan keeps workgroup order: its 512 KiB items
+// measured 5 % slower with this mapping.)
+constexpr uint32_t kXcdRun = 16;
 
-__device__ __forceinline__ uint32_t xcd_item(uint32_t b, uint32_t n) {
-  constexpr uint32_t kWin = kXcds * kXcdRun;
-  if (b >= n / kWin * kWin) return b;
-  const uint32_t o = b % kWin;
-  return (b - o) + (o % kXcds) * kXcdRun + o / kXcds;
+__device__ __forceinline__ uint32_t xcd_item(uint32_t b, uint32_t n, uint32_t xcds) {
+  const uint32_t win = xcds * kXcdRun;
+  if (xcds <= 1u || b >= n / win * win) return b;
+  const uint32_t o = b % win;
+  return (b - o) + (o % xcds) * kXcdRun + o / xcds;
 }
 
 // Index of the calling wave over the grid (4*block + wave), wave-uniform.

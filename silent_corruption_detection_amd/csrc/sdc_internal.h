@@ -123,6 +123,17 @@ inline uint32_t element_size(uint32_t dtype) {
   }
 }
 
+// Shape of the device a call runs on (csrc/device.cpp): its compute units and
+// XCDs.  Work splits that aim at "one item per CU" use `cus`; the list scans'
+// workgroup-to-item map uses `xcds`.  gfx950 XCDs hold kCusPerXcd active CUs.
+constexpr uint32_t kCusPerXcd = 32;
+struct DeviceShape {
+  uint32_t cus, xcds;
+};
+uint32_t xcds_of(uint32_t cus);
+// Shape of the calling thread's current device (queried once per device).
+int32_t current_device_shape(DeviceShape* out);
+
 // Thread-local record of the last failing HIP call.
 void set_hip_error(hipError_t e);
 

@@ -2,150 +2,31 @@
 // on-device compare against a stored row: the recompute check of the AEGIS
 // review page ("Safeguarding LLM Training at Scale"), section "core method",
 // item 4 (fingerprints of an original and of its deterministic
-// recomputation, compared bit for bit), for gfx950.
-#include <algorithm>
-
-#include "fingerprint_device.h"
-
-namespace sdc {
-namespace {
-
-// ---- one tensor, no plan ---------------------------------------------------------
-// The items of a single tensor follow from the workgroup index alone (the same
-// split a plan makes): item 0 covers the misaligned head and the next ie
-// elements, item i >= 1 the elements [h + i*ie, h + (i+1)*ie).  So the scan
-// needs no plan upload and no host synchronisation.  Every item stores its
-// partial row in slot i of the caller's workspace; one wave merges them.
-struct TensorJob {
-  uint64_t addr, numel, ie;  // base address, elements, elements per item
-  uint32_t h, df;            // misaligned head elements; dtype | kItemSigned
-  uint32_t es, pad;
-};
-
-__device__ __forceinline__ PlanItem job_item(const TensorJob& j, uint32_t i) {
-  const uint64_t start = i ? j.h + (uint64_t)i * j.ie : 0u;
-  const uint64_t end = min(j.numel, (uint64_t)j.h + (uint64_t)(i + 1) * j.ie);
-  PlanItem it;
-  it.addr = j.addr + start * j.es;
-  it.start = start;
-  it.len = (uint32_t)(end - start);
-  it.row = 0;
-  it.slot = i;
-  it.dtype_flags = j.df;
-  return it;
-}
-
-template <class Cfg>
-__global__ void __launch_bounds__(kBlock) fingerprint_tensor_kernel(TensorJob j,
-                                                                    sdc_row* __restrict__ partials) {
-  const PlanItem it = job_item(j, blockIdx.x);
-  Lane ln;
-  dispatch_type(it.dtype_flags, [&](auto ty) { scan_item<decltype(ty), Cfg>(it, ln); });
-  if (threadIdx.x != 0) return;
-  ulonglong2* d = reinterpret_cast<ulonglong2*>(partials + blockIdx.x);
-  d[0] = ulonglong2{ln.s, ln.w + it.start * ln.s};
-  d[1] = ulonglong2{ln.x, ln.nf};
-}
-
-__device__ __forceinline__ bool rows_differ(const sdc_row& a, const sdc_row& b, uint32_t mask) {
-  return ((mask & SDC_COL_SUM) && a.sum != b.sum) || ((mask & SDC_COL_WSUM) && a.wsum != b.wsum) ||
-         ((mask & SDC_COL_XOR) && a.xorsum != b.xorsum) ||
-         ((mask & SDC_COL_NONFINITE) && a.nonfinite != b.nonfinite);
-}
-
-// One workgroup: the tensor's row from its n partial rows; with a reference
-// row, a difference under the mask adds 1 to *mismatch.
-__global__ void __launch_bounds__(kBlock) merge_check_kernel(const sdc_row* __restrict__ partials,
-                                                             uint32_t n, sdc_row* __restrict__ out,
-                                                             const sdc_row* __restrict__ ref,
-                                                             uint32_t mask,
-                                                             uint32_t* __restrict__ mismatch) {
-  Lane ln = merge_slots<kBlock>(partials, n, threadIdx.x);
-  block_reduce(ln);
-  if (threadIdx.x != 0) return;
-  const sdc_row r{ln.s, ln.w, ln.x, ln.nf};
-  ulonglong2* d = reinterpret_cast<ulonglong2*>(out);
-  d[0] = ulonglong2{r.sum, r.wsum};
-  d[1] = ulonglong2{r.xorsum, r.nonfinite};
-  if (ref && rows_differ(r, *ref, mask)) atomicAdd(mismatch, 1u);
-}
-
-// Automatic item size of the single-tensor scan.  A call scans one tensor, so
-// the launch's start and tail weigh more than in a list scan.  Tensors of at
-// least kTensorWideMin bytes are cut into a multiple of kCUs items (one item
-// per CU per pass, at most kItemBytesMax each) and scanned in the tensor-wide
-// shape: one workgroup per CU (LDS reservation), non-pipelined rounds of 8
-// vectors per lane.  Measured per call on bf16 activations (one box): 512 MiB
-// 77.5 us (6.92 TB/s) against 82 us with ~1024 items of 512 KiB in the deep
-// shape; 256 MiB 42.0 vs 44.1 us; 128 MiB 24.4 vs 26.2 us; 12 vectors per
-// round 1-3 % slower, two items per CU 2-5 % slower.  Smaller tensors take
-// about kTensorTargetItems items (four per CU) within [kAutoMin, kAutoMax]
-// (measured on 512 MiB tensors in the deep shape: 64 KiB items 5.7 TB/s,
-// 256 KiB 6.5, 512 KiB - 2 MiB 6.5-6.6, 4 MiB 5.6).
-constexpr uint64_t kCUs = 256;
-constexpr uint64_t kTensorWideMin = 128ull << 20;
-constexpr uint64_t kTensorTargetItems = 1024;
-typedef BodyCfg<8, false> TensorWideBody;
-
-uint64_t round_4k(uint64_t b) { return (b + 4095) / 4096 * 4096; }
-
-uint64_t tensor_item_bytes(uint64_t bytes) {
-  if (bytes >= kTensorWideMin) {
-    const uint64_t passes = (bytes + kCUs * kItemBytesMax - 1) / (kCUs * kItemBytesMax);
-    const uint64_t items = kCUs * passes;
-    return round_4k((bytes + items - 1) / items);  // <= kItemBytesMax, a multiple of 4 KiB
-  }
-  const uint64_t ib = round_4k(std::max<uint64_t>(bytes / kTensorTargetItems, 1));
-  return ib < kAutoMin ? kAutoMin : (ib > kAutoMax ? kAutoMax : ib);
-}
-
-// Launch shape of the single-tensor scan: items, the split of item 0, and
-// whether the items are few and large enough for the tensor-wide shape (at
-// most two per CU of at least 512 KiB: what the automatic size gives tensors
-// of 128 MiB - 1 GiB; larger ones, several passes of 4 MiB items, also take it).
-struct TensorShape {
-  uint64_t n_items, ie;
-  uint32_t h, es;
-  bool wide;
-};
-
-int32_t tensor_shape(const sdc_tensor* t, uint64_t item_bytes, TensorShape* sh) {
-  if (t == nullptr) return SDC_ERR_INVALID;
-  if (item_bytes % kVecBytes != 0 || item_bytes > kItemBytesMax) return SDC_ERR_INVALID;
-  if ((t->flags & ~(uint32_t)SDC_FLAG_SIGNED) != 0) return SDC_ERR_INVALID;
-  const uint32_t es = element_size(t->dtype);
-  if (es == 0) return SDC_ERR_DTYPE;
-  if (t->numel >= (1ull << 62) / es) return SDC_ERR_RANGE;  // bytes < 2^62
-  const uint64_t numel = t->ptr ? t->numel : 0u;
-  const uint64_t ptr = reinterpret_cast<uintptr_t>(t->ptr);
-  if (ptr % es != 0) return SDC_ERR_ALIGN;
-  const uint64_t ie = (item_bytes ? item_bytes : tensor_item_bytes(numel * es)) / es;
-  const uint64_t mis = ptr & 15u;
-  const uint64_t h = mis ? std::min<uint64_t>(numel, (16u - mis) / es) : 0u;
-  const uint64_t first = std::min<uint64_t>(numel, h + ie);
-  sh->n_items = numel ? 1 + (numel - first + ie - 1) / ie : 0;
-  if (sh->n_items > kMaxGrid) return SDC_ERR_RANGE;
-  sh->ie = ie;
-  sh->h = (uint32_t)h;
-  sh->es = es;
-  const uint64_t ib = ie * es;
-  sh->wide = ib >= (512ull << 10) &&
-             (sh->n_items <= 2 * kCUs || (item_bytes == 0 && numel * es >= kTensorWideMin));
-  return SDC_OK;
-}
-
-}  // namespace
-}  // namespace sdc
+// recomputation, compared bit for bit), for gfx950.  The partial rows of the
+// tensor's work items live in a caller workspace.
+#include "tensor_device.h"
 
 using namespace sdc;
 
 extern "C" int32_t sdc_tensor_ws_bytes(const sdc_tensor* h_tensor, uint64_t item_bytes,
                                        uint64_t* h_bytes) {
   if (h_bytes == nullptr) return SDC_ERR_INVALID;
-  TensorShape sh;
-  const int32_t st = tensor_shape(h_tensor, item_bytes, &sh);
+  uint64_t slots = 0;
+  const int32_t st = tensor_slots_bound(h_tensor, item_bytes, &slots);
   if (st) return st;
-  *h_bytes = std::max<uint64_t>(sh.n_items, 1) * sizeof(sdc_row);
+  *h_bytes = slots * sizeof(sdc_row);
+  return SDC_OK;
+}
+
+extern "C" int32_t sdc_tensor_split_host(const sdc_tensor* h_tensor, uint64_t item_bytes,
+                                         uint32_t cu_count, uint64_t* h_n_items,
+                                         uint64_t* h_item_bytes) {
+  if (h_n_items == nullptr || h_item_bytes == nullptr || cu_count == 0) return SDC_ERR_INVALID;
+  TensorShape sh;
+  const int32_t st = tensor_shape(h_tensor, item_bytes, cu_count, &sh);
+  if (st) return st;
+  *h_n_items = sh.n_items;
+  *h_item_bytes = sh.ie * sh.es;
   return SDC_OK;
 }
 
@@ -153,35 +34,14 @@ extern "C" int32_t sdc_fingerprint_tensor(const sdc_tensor* h_tensor, uint64_t i
                                           uint64_t ws_bytes, const sdc_row* d_ref, uint32_t col_mask,
                                           sdc_row* d_out, uint32_t* d_mismatch, sdc_stream_t stream) {
   TensorShape sh;
-  int32_t st = tensor_shape(h_tensor, item_bytes, &sh);
+  int32_t st = tensor_shape(h_tensor, item_bytes, kMaxSplitCus, &sh);  // argument checks first
   if (st) return st;
-  if (d_out == nullptr || d_ws == nullptr) return SDC_ERR_INVALID;
-  if (d_ref && (d_mismatch == nullptr || (col_mask & SDC_COL_ALL) == 0 ||
-                (col_mask & ~(uint32_t)SDC_COL_ALL) != 0))
-    return SDC_ERR_INVALID;
+  if ((st = check_tensor_call(d_ref, col_mask, d_out, d_mismatch))) return st;
+  if (d_ws == nullptr) return SDC_ERR_INVALID;
+  DeviceShape dev;
+  if ((st = current_device_shape(&dev))) return st;
+  if ((st = tensor_shape(h_tensor, item_bytes, dev.cus, &sh))) return st;
   if (ws_bytes < std::max<uint64_t>(sh.n_items, 1) * sizeof(sdc_row)) return SDC_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
-  sdc_row* partials = reinterpret_cast<sdc_row*>(d_ws);
-  if (sh.n_items) {
-    TensorJob j;
-    j.addr = reinterpret_cast<uintptr_t>(h_tensor->ptr);
-    j.numel = h_tensor->numel;
-    j.ie = sh.ie;
-    j.h = sh.h;
-    j.df = h_tensor->dtype | ((h_tensor->flags & SDC_FLAG_SIGNED) ? kItemSigned : 0u);
-    j.es = sh.es;
-    j.pad = 0;
-    const dim3 grid((uint32_t)sh.n_items), block(kBlock);
-    if (sh.wide)
-      hipLaunchKernelGGL(fingerprint_tensor_kernel<TensorWideBody>, grid, block, kWideLdsBytes, s, j,
-                         partials);
-    else if (sh.ie * sh.es >= kDeepItemBytes)
-      hipLaunchKernelGGL(fingerprint_tensor_kernel<DeepBody>, grid, block, 0, s, j, partials);
-    else
-      hipLaunchKernelGGL(fingerprint_tensor_kernel<DefaultBody>, grid, block, 0, s, j, partials);
-    if ((st = launch_status())) return st;
-  }
-  hipLaunchKernelGGL(merge_check_kernel, dim3(1), dim3(kBlock), 0, s, partials,
-                     (uint32_t)sh.n_items, d_out, d_ref, col_mask, d_mismatch);
-  return launch_status();
+  return launch_tensor(h_tensor, sh, reinterpret_cast<sdc_row*>(d_ws), d_ref, col_mask, d_out,
+                       d_mismatch, as_stream(stream));
 }

@@ -170,28 +170,64 @@ def test_tensor_ws_bytes_match_the_plan_split(desc, item_bytes):
     assert ws == 32 * one_tensor_plan_items(desc, item_bytes)[0]
 
 
-def auto_tensor_item_bytes(nbytes):
-    # tensors of at least 128 MiB: a multiple of 256 items (one per CU per pass)
-    # of at most 4 MiB; smaller ones: about 1024 items within [64 KiB, 1 MiB];
-    # item sizes are multiples of 4 KiB
+def tensor_split(desc, item_bytes, cus):
+    import silent_corruption_detection_amd as sdc
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    t = _T(*desc)
+    n, ib = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    rc = lib.sdc_tensor_split_host(ctypes.byref(t), ctypes.c_uint64(item_bytes), ctypes.c_uint32(cus),
+                                   ctypes.byref(n), ctypes.byref(ib))
+    return rc, n.value, ib.value
+
+
+def auto_tensor_item_bytes(nbytes, cus=256):
+    # tensors of at least 128 MiB: a multiple of `cus` items (one per CU per
+    # pass; at most 256 CUs are used) of at most 4 MiB; smaller ones: about
+    # 1024 items within [64 KiB, 1 MiB]; item sizes are multiples of 4 KiB
     r4k = lambda b: -(-b // 4096) * 4096
+    c = max(1, min(cus, 256))
     if nbytes >= 128 << 20:
-        passes = -(-nbytes // (256 * (4 << 20)))
-        return r4k(-(-nbytes // (256 * passes)))
+        passes = -(-nbytes // (c * (4 << 20)))
+        return r4k(-(-nbytes // (c * passes)))
     return min(max(r4k(max(nbytes // 1024, 1)), 64 << 10), 1 << 20)
 
 
+ESZ = {0: 4, 1: 2, 2: 2, 3: 8, 4: 1}
+
+
 @pytest.mark.parametrize("desc", DESCS)
-def test_tensor_automatic_item_size(desc):
-    nbytes = desc[1] * {0: 4, 1: 2, 2: 2, 3: 8, 4: 1}[desc[2]]
-    ib = auto_tensor_item_bytes(nbytes)
+@pytest.mark.parametrize("cus", [256, 80, 32, 1, 304])
+def test_tensor_automatic_item_size(desc, cus):
+    # the split on a device with `cus` compute units (the full MI355X: 256; a
+    # CPX partition: 32), and the workspace bound that holds for all of them
+    nbytes = desc[1] * ESZ[desc[2]]
+    ib = auto_tensor_item_bytes(nbytes, cus)
     assert ib % 4096 == 0 and ib <= 4 << 20
+    rc, n_split, ib_split = tensor_split(desc, 0, cus)
+    assert rc == 0 and ib_split == ib
     n_items, total = one_tensor_plan_items(desc, ib)
-    assert total == nbytes
-    assert tensor_ws_bytes(desc)[1] == 32 * n_items
+    assert total == nbytes and n_split == n_items
+    assert tensor_ws_bytes(desc)[1] >= 32 * n_items
+    c = max(1, min(cus, 256))
     if nbytes >= 128 << 20:  # one item per CU per pass, at most 4 MiB each
-        passes = -(-nbytes // (256 * (4 << 20)))
-        assert 256 * passes - 256 < n_items <= 256 * passes
+        passes = -(-nbytes // (c * (4 << 20)))
+        assert c * passes - c < n_items <= c * passes + 1
+    else:  # the workspace is exact below the wide split
+        assert tensor_ws_bytes(desc)[1] == 32 * n_items
+
+
+@pytest.mark.parametrize("desc", DESCS)
+def test_tensor_ws_bound_covers_every_cu_count(desc):
+    ws = tensor_ws_bytes(desc)[1]
+    nbytes = desc[1] * ESZ[desc[2]]
+    worst = max(tensor_split(desc, 0, c)[1] for c in range(1, 257))
+    assert 32 * worst <= ws <= 32 * max(worst, -(-nbytes // (4 << 20)) + 257)
+
+
+def test_tensor_split_explicit_item_size_ignores_cus():
+    for cus in (1, 32, 256):
+        assert tensor_split((0x10002, 3 << 20, 1, 0), 65536, cus) == (0, 96, 65536)
+    assert tensor_split((0x10000, 10, 0, 0), 0, 0)[0] == -1
 
 
 @pytest.mark.parametrize("desc,item_bytes,code", [

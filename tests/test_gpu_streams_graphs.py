@@ -144,3 +144,29 @@ def test_graph_capture_and_replay(ib):
         assert got[5] == int(e_flag.item()) == 1    # the list holds a NaN
         assert np.array_equal(got[6], e_one)
         assert got[7] == (1 if rep >= 2 else 0)
+
+
+def test_strided_inputs_scanned_on_a_side_stream():
+    # The binding makes contiguous copies of strided inputs (and allocates
+    # the workspace and output) on the current stream; a scan on another
+    # stream must still read the finished copies.  The copies are made right
+    # after a long kernel on the current stream, so a side stream that did not
+    # wait would run ahead of them.
+    g = gen(11)
+    base = [torch.empty((2048, 3000), dtype=torch.float32, device=DEV).normal_(0, 0.02, generator=g),
+            torch.empty((777, 4096), dtype=torch.bfloat16, device=DEV).normal_(0, 0.02, generator=g)]
+    views = [base[0].t(), base[1][:, ::3], base[0][5:, 1::2].t()]
+    assert not any(v.is_contiguous() for v in views)
+    ref = oracle_rows([v.contiguous() for v in views])
+    big = torch.empty(1 << 28, dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"case strided side stream rep={rep}")
+        big.add_(1.0)  # keeps the current stream busy while the copies are enqueued behind it
+        rows = sdc.sdc_fingerprint(views, stream=side)
+        one = [sdc.sdc_fingerprint_tensor(v, stream=side) for v in views]
+        side.synchronize()
+        assert_rows_equal(sdc.rows_numpy(rows), ref)
+        assert_rows_equal(np.concatenate([sdc.rows_numpy(o) for o in one]), ref)
+    torch.cuda.synchronize()

@@ -109,16 +109,23 @@ def test_localize_brute_force():
 
 
 def test_verdict_table_exhaustive():
+    # Each verdict row of "Decide what the alarm means" as a statement about
+    # the four results, checked over every assignment of three values.
     vals = [np.full(3, v, dtype=np.uint64) for v in (1, 2, 3)]
-    for third, self_, orig, peer in itertools.product(range(3), repeat=4):
-        got = O.VERDICTS[O.confirm_verdict(vals[third], vals[self_], vals[orig], vals[peer])]
-        if third == orig:
+    for witness, retry, original, replay in itertools.product(range(3), repeat=4):
+        got = O.VERDICTS[O.confirm_verdict(vals[witness], vals[retry], vals[original], vals[replay])]
+        sided_with_replayer = witness == replay and witness != original
+        if witness == original:  # "the replaying GPU, not the target, was wrong"
             want = "replayer computed wrong"
-        elif third == peer:
-            want = "persistent" if self_ == orig else "transient" if self_ == third else "unclear"
+        elif sided_with_replayer and retry == original:  # "reproduced its own wrong answer"
+            want = "persistent"
+        elif sided_with_replayer and retry == witness:  # "retry came out right and agreed"
+            want = "transient"
+        elif sided_with_replayer:  # the three do not line up
+            want = "unclear"
         else:
             want = "unattributable"
-        assert got == want
+        assert got == want, (witness, retry, original, replay)
 
 
 def test_library_localize_matches_oracle_host_only():
