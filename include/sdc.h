@@ -23,8 +23,10 @@
  *   - "d_" arguments are device pointers (HIP device memory of the current
  *     device), "h_" arguments are host pointers.  The caller owns and allocates
  *     all device memory; the library allocates none.  Between calls it keeps
- *     only per-host-thread state: the last HIP error and a small host staging
- *     buffer of the compare calls' single device-to-host copy.
+ *     only per-host-thread state (the last HIP error and a small host staging
+ *     buffer of the compare calls' single device-to-host copy), per-device
+ *     facts (the compute-unit count), and one static 256 KiB device array per
+ *     GPU that only sdc_fingerprint_tensor_noalloc uses.
  *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
  *     Functions documented as asynchronous only enqueue work on that stream;
  *     their device outputs are valid once the stream reaches that point.
@@ -291,6 +293,26 @@ int32_t sdc_tensor_split_host(const sdc_tensor* h_tensor, uint64_t item_bytes, u
 int32_t sdc_fingerprint_tensor(const sdc_tensor* h_tensor, uint64_t item_bytes, void* d_ws,
                                uint64_t ws_bytes, const sdc_row* d_ref, uint32_t col_mask,
                                sdc_row* d_out, uint32_t* d_mismatch, sdc_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the scan of
+ * sdc_fingerprint_tensor -- same arguments, same row, same compare -- without
+ * a workspace.  The partial rows of the tensor's work items go to a static
+ * device array of 8192 rows (256 KiB) that the library holds on every GPU it
+ * runs on until the process ends; no device memory is allocated by the call.
+ * Limit: the tensor's split must fit the array on every device -- at most
+ * 8192 work items for an explicit item_bytes; with the automatic split
+ * (item_bytes 0), tensors of up to 7935 * 4 MiB (about 31 GiB).  Larger ones
+ * give SDC_ERR_RANGE before anything is queued.  All calls on one GPU share
+ * the array: calls that overlap in time on one GPU (on different streams or
+ * from different host threads) race and give wrong rows; calls in order on
+ * one stream are safe (each call's items write their slots before its merge
+ * reads them, so the array needs no clearing).  ASYNCHRONOUS on stream, like
+ * sdc_fingerprint_tensor.  Errors as sdc_fingerprint_tensor, with
+ * SDC_ERR_RANGE for a tensor beyond the limit. */
+int32_t sdc_fingerprint_tensor_noalloc(const sdc_tensor* h_tensor, uint64_t item_bytes,
+                                       const sdc_row* d_ref, uint32_t col_mask, sdc_row* d_out,
+                                       uint32_t* d_mismatch, sdc_stream_t stream);
 
 /* ---- comparisons of fingerprint tables ------------------------------------ */
 

@@ -23,6 +23,7 @@ __all__ = [
     "sdc_abi_version", "rows_numpy", "LIB_PATH", "sdc_ring_ws_bytes", "sdc_ring_compare",
     "sdc_ring_localize", "sdc_confirm_verdict", "VERDICTS", "sdc_sqnorm",
     "sdc_tensor_ws_bytes", "sdc_tensor_split_host", "sdc_fingerprint_tensor",
+    "sdc_fingerprint_tensor_noalloc",
     "sdc_read_sum_ws_bytes", "sdc_read_sum",
 ]
 
@@ -88,6 +89,7 @@ def _load():
         "sdc_tensor_ws_bytes": [P, U64, P],
         "sdc_tensor_split_host": [P, U64, U32, P, P],
         "sdc_fingerprint_tensor": [P, U64, P, U64, P, U32, P, P, P],
+        "sdc_fingerprint_tensor_noalloc": [P, U64, P, U32, P, P, P],
         "sdc_ring_ws_bytes": [U32, P],
         "sdc_ring_compare": [P, U32, U64, U32, P, U64, P, P],
         "sdc_ring_localize": [P, U32, U32, P, P],
@@ -425,6 +427,33 @@ def sdc_fingerprint_tensor(t, out=None, ref=None, mismatch=None, col_mask=COL_AL
                                        ctypes.c_void_p(ref_p), col_mask,
                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(mis_p),
                                        ctypes.c_void_p(s.cuda_stream)), "sdc_fingerprint_tensor")
+    return out
+
+
+def sdc_fingerprint_tensor_noalloc(t, out, ref=None, mismatch=None, col_mask=COL_ALL,
+                                   stream=None, signed=False, item_bytes=0):
+    """sdc_fingerprint_tensor without a workspace: the library keeps the
+    partial rows in a static device array (at most 8192 work items, so
+    tensors of up to about 31 GiB with the automatic split).  `out` (a device
+    int64 row, e.g. a row of a table) and a contiguous `t` keep this call
+    free of device allocations; calls that overlap in time on one GPU race."""
+    desc, dev, keep = _one_descriptor(t, signed)
+    if dev is None:
+        dev = torch.device("cuda")
+    _arg(out, "out", torch.int64, 4, dev)
+    ref_p = mis_p = None
+    if ref is not None:
+        _arg(ref, "ref", torch.int64, 4, dev)
+        if mismatch is None:
+            raise ValueError("a compare needs a one-element int32 mismatch counter")
+        _arg(mismatch, "mismatch", torch.int32, 1, dev)
+        ref_p, mis_p = ref.data_ptr(), mismatch.data_ptr()
+    s = _scan_stream(stream, dev, [x for x in keep if x is not t])
+    _check(_lib.sdc_fingerprint_tensor_noalloc(ctypes.byref(desc), item_bytes, ctypes.c_void_p(ref_p),
+                                               col_mask, ctypes.c_void_p(out.data_ptr()),
+                                               ctypes.c_void_p(mis_p),
+                                               ctypes.c_void_p(s.cuda_stream)),
+           "sdc_fingerprint_tensor_noalloc")
     return out
 
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsdc.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "libsdc")
 SOURCES = ["scan.hip", "tensor.hip", "nonfinite.hip", "norm.hip", "compare.hip", "readsum.hip",
-           "plan.cpp", "device.cpp", "misc.cpp"]
+           "noalloc.hip", "plan.cpp", "device.cpp", "misc.cpp"]
 ARCH = os.environ.get("SDC_OFFLOAD_ARCH", "gfx950")
 NOISE = "is not a recognized feature for this target"
 
