@@ -49,9 +49,12 @@ def lib():
     """Load the oracle library, building it with gcc if it is not there yet."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        path = os.environ.get("SDC_ORACLE_LIB")  # e.g. the sanitizer build
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         P, U64, U32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
         L.oracle_element_size.argtypes = [U32]
         L.oracle_element_size.restype = U32

@@ -27,7 +27,10 @@ __all__ = [
     "sdc_read_sum_ws_bytes", "sdc_read_sum",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
+# The in-tree build; SDC_LIB_PATH may name another build of the same sources
+# (the sanitizer build of the host code, for CPU test runs).
+LIB_PATH = os.environ.get("SDC_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libsdc.so")
 ABI_VERSION = 2  # SDC_ABI_VERSION of include/sdc.h that the structs below mirror
 
 (F32, BF16, F16, F64, U8, FP8_E4M3, FP8_E5M2, FP8_E4M3FNUZ, FP8_E5M2FNUZ, U16, U32,

@@ -13,11 +13,12 @@ from the oracle, never from the HIP path:
           gives the flipped element and bit.
   c4      rows equal the oracle's for all 300,000 tensors; the named replicas
           are those the corruptions went to.
-  c5      (141 GB) rows of a sample of tensors equal the oracle's, and so do
-          their squared norms (within the summation bound); no NaN/Inf is
-          counted and the norm check is clear; a second scan is identical to
-          the first (diff empty); one seeded flip gives exactly one differing
-          tensor with the exact localisation.
+  c5      (141 GB) all 723 rows equal the oracle's (the oracle's table is
+          the stored table: a second scan diffed against it is empty); the
+          NaN/Inf counts equal the oracle's (all zero) and the norm check is
+          clear; squared norms of a sample of tensors equal the oracle's
+          (within the summation bound); one seeded flip gives exactly one
+          differing tensor with the exact localisation.
 """
 import gc
 
@@ -28,7 +29,9 @@ import torch
 import oracle as O
 import silent_corruption_detection_amd as sdc
 import workloads as W
-from _util import assert_rows_equal, assert_sq_close, oracle_nonfinite, oracle_rows, oracle_sqnorms, say
+from _util import (THREADS, assert_rows_equal, assert_sq_close, oracle_nonfinite, oracle_rows,
+                   oracle_sqnorms, say)
+from oracle.device_lists import rows_of_device_tensors
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -137,29 +140,39 @@ def test_c5_llama70b_bf16():
     assert w.elems_per_replica == 70_553_706_496
     plan, out = scan(w)
     first = out.clone()
-    sample = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 365, 366, 367, 368, 369, 370, 371, 721, 722]
-    say("case c5: oracle on a sample of tensors")
-    assert_rows_equal(sdc.rows_numpy(out)[sample], oracle_rows([w.tensors[k] for k in sample]),
-                      [w.names[k] for k in sample])
+    # every one of the 723 rows against the oracle (streamed to the host
+    # through pinned buffers, 16 oracle calls at a time): the table stored
+    # after a checkpoint, computed by the oracle
+    say("case c5: oracle over all 723 tensors")
+    ref, st = rows_of_device_tensors(w.tensors, threads=THREADS)
+    say(f"case c5: oracle done: {st['bytes'] / 1e9:.1f} GB in {st['wall_s']:.1f} s "
+        f"(copies {st['d2h_s']:.1f} s)")
+    assert st["bytes"] == plan.total_bytes
+    assert_rows_equal(sdc.rows_numpy(out), ref, w.names)
+    stored = torch.from_numpy(ref.view(np.int64)).to(DEV)
     # the NaN/Inf-count and squared-norm scans on the same list (wide launch shape)
     say("case c5: NaN/Inf counts and squared norms")
     counts, total = sdc.sdc_nonfinite(plan)
     sq, sq_total, flag = sdc.sdc_sqnorm(plan)
     torch.cuda.synchronize()
-    assert int(total.item()) == 0 and int(counts.sum().item()) == 0
+    assert counts.cpu().numpy().astype(np.uint64).tolist() == ref[:, 3].tolist()
+    assert int(total.item()) == 0 == int(ref[:, 3].sum())
     assert int(flag.item()) == 0
+    sample = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 365, 366, 367, 368, 369, 370, 371, 721, 722]
     picked = [w.tensors[k] for k in sample]
     assert_sq_close(sq.cpu().numpy()[sample].tolist(), oracle_sqnorms(picked),
                     [t.numel() for t in picked])
+    # the check after a restore: a second scan diffed against the oracle's table
     sdc.sdc_fingerprint_plan(plan, out)
-    d = sdc.sdc_fingerprint_diff(first, out)
+    d = sdc.sdc_fingerprint_diff(stored, out)
     assert d["n_diff"] == 0
+    assert torch.equal(out, first)
     inj = W.c5_flip(w)
     say(f"case c5: flip {inj}")
     sdc.sdc_fingerprint_plan(plan, out)
-    d = sdc.sdc_fingerprint_diff(first, out)
+    d = sdc.sdc_fingerprint_diff(stored, out)
     assert d["n_diff"] == 1 and d["indices"] == [inj["tensor"]]
     assert d["hints"] == [(inj["index"], inj["bit"], -1 if inj["was"] else 1)]
     k = inj["tensor"]
     assert_rows_equal(sdc.rows_numpy(out)[[k]], oracle_rows([w.tensors[k]]), [w.names[k]])
-    del w, plan, out, first
+    del w, plan, out, first, stored

@@ -97,8 +97,13 @@ def test_tensor_empty_missing_and_large():
     t = torch.empty(128256 * 8192, dtype=torch.bfloat16, device=DEV).normal_(0, 0.02, generator=g)
     plan = sdc.sdc_plan_build([t])
     a = sdc.rows_numpy(sdc.sdc_fingerprint_plan(plan))
-    assert one_row(t).tolist() == a.tolist()
-    # and equals the oracle on a slice that spans items and a ragged tail
+    # the whole tensor against the oracle (2.1 GB, one oracle call), and the
+    # list scan of the same tensor
+    say("case tensor 2 GiB bf16: oracle over the whole tensor")
+    ref = oracle_rows([t])
+    assert_rows_equal(one_row(t), ref)
+    assert_rows_equal(a, ref)
+    # and a slice that spans items and a ragged tail
     s = t[:3_000_001]
     assert_rows_equal(one_row(s), oracle_rows([s]))
     del t, plan
