@@ -142,12 +142,7 @@ def one_tensor_plan_items(desc, item_bytes):
                               ctypes.byref(need)) == 0
     buf = (ctypes.c_ubyte * need.value)()
 
-    class Info(ctypes.Structure):
-        _fields_ = [(n, ctypes.c_uint64) for n in ("magic", "n_tensors", "n_items", "n_small",
-                                                    "n_split", "n_slots", "total_elems",
-                                                    "total_bytes", "plan_bytes", "item_bytes")
-                    ] + [("n_wave", ctypes.c_uint64 * 4)]
-    info = Info()
+    info = sdc._PlanInfo()
     assert lib.sdc_plan_pack_host(arr, ctypes.c_uint64(1), ctypes.c_uint64(item_bytes), buf,
                                   ctypes.c_uint64(need.value), ctypes.byref(info)) == 0
     return info.n_items, info.total_bytes

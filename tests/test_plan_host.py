@@ -129,6 +129,30 @@ def check_plan(descs, item_bytes):
     return info
 
 
+def flat_list(rng, n, base=0x7F0000000000, gap_max=3, dts=(0, 1, 2), max_numel=65536):
+    """Tensors carved back to back from one flat buffer at element-aligned
+    offsets (plus random gaps of up to gap_max bytes), like gradient-bucket views."""
+    descs, off = [], 0
+    for _ in range(n):
+        dt = int(rng.choice(dts))
+        es = ES[dt]
+        numel = min(max_numel, int(np.exp(rng.uniform(0, np.log(max_numel + 1)))))
+        off += int(rng.integers(0, gap_max + 1))
+        off = -(-off // es) * es
+        descs.append((base + off, numel, dt, int(rng.integers(0, 2))))
+        off += numel * es
+    return descs
+
+
+@pytest.mark.parametrize("item_bytes", [0, 4096, 1 << 20])
+def test_flat_buffer_lists_are_covered_exactly(item_bytes):
+    # neighbouring tensors share 16-byte vectors; each is still covered
+    # exactly by its own items, whose heads and tails are read element-wise
+    rng = np.random.default_rng(item_bytes + 7)
+    check_plan(flat_list(rng, 2000, dts=(0, 1, 2, 3, 4, 5, 9, 10, 11)), item_bytes)
+    check_plan(flat_list(rng, 1000, max_numel=3), item_bytes)
+
+
 @pytest.mark.parametrize("item_bytes", [0, 16, 48, 4096, 65536, 1 << 20, 4 << 20])
 def test_random_lists_are_covered_exactly(item_bytes):
     rng = np.random.default_rng(item_bytes + 1)
