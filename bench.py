@@ -46,18 +46,23 @@ def kernel_hash():
 
 
 def traffic_from_profile(workload):
-    """HBM bytes per scan launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+    """(HBM bytes per scan launch, cross-check) from the committed counter
+    summary, if it was taken on the current kernel source; else (None, None).
+    The bytes are FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what
+    the same counter reads for an elementwise kernel of known size; the
+    cross-check gives the read bytes from two independent counter sets (EA
+    read requests by size, and DRAM read requests in 32-byte units) over the
+    scaled FETCH_SIZE."""
     path = os.path.join(ROOT, "profiles", f"fingerprint_kernel_{workload}_pmc.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     try:
         d = json.load(open(path))
     except ValueError:
-        return None
+        return None, None
     if d.get("kernel_hash") != kernel_hash():
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return None, None
+    return d.get("hbm_bytes_per_launch"), d.get("read_cross_check")
 
 
 def profiled_time(workload, total_bytes):
@@ -433,7 +438,7 @@ def main():
     torch.cuda.empty_cache()
     total_bytes = plan.total_bytes
     achieved = total_bytes / kms / 1e6  # GB/s
-    traffic = traffic_from_profile("llama70b_bf16")
+    traffic, traffic_check = traffic_from_profile("llama70b_bf16")
     ceiling = read_ceiling(args, torch, sdc)
     value = total_bytes / ms / 1e6
     line = {
@@ -448,7 +453,9 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "fingerprint_kernel (+ merge_rows_kernel)",
+                     "traffic": traffic,
+                     "traffic_read_cross_check": traffic_check,
+                     "kernel": "fingerprint_kernel (+ merge_rows_kernel)",
                      "kernel_ms": round(kms, 4), "kernel_hash": kernel_hash(),
                      "timing": "HIP events on the launch stream, this run",
                      "profiled": profiled_time("llama70b_bf16", total_bytes),
