@@ -32,6 +32,7 @@ import workloads as W
 from _util import (THREADS, assert_rows_equal, assert_sq_close, oracle_nonfinite, oracle_rows,
                    oracle_sqnorms, say)
 from oracle.device_lists import rows_of_device_tensors
+from silent_corruption_detection_amd.table import load_table, save_table
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -134,7 +135,7 @@ def test_c4_small_mixed_tensors():
     assert res["first_diff"] == min(i["tensor"] for i in w.injections)
 
 
-def test_c5_llama70b_bf16():
+def test_c5_llama70b_bf16(tmp_path):
     say("case c5: generate 141 GB")
     w = W.c5(DEV)
     assert w.elems_per_replica == 70_553_706_496
@@ -149,7 +150,11 @@ def test_c5_llama70b_bf16():
         f"(copies {st['d2h_s']:.1f} s)")
     assert st["bytes"] == plan.total_bytes
     assert_rows_equal(sdc.rows_numpy(out), ref, w.names)
-    stored = torch.from_numpy(ref.view(np.int64)).to(DEV)
+    # saved beside the checkpoint, loaded back after the restore (checked
+    # against the live list's types and sizes)
+    save_table(str(tmp_path / "c5"), torch.from_numpy(ref.view(np.int64)), w.tensors, names=w.names)
+    stored, _ = load_table(str(tmp_path / "c5"), tensors=w.tensors, device=DEV)
+    assert np.array_equal(sdc.rows_numpy(stored), ref)
     # the NaN/Inf-count and squared-norm scans on the same list (wide launch shape)
     say("case c5: NaN/Inf counts and squared norms")
     counts, total = sdc.sdc_nonfinite(plan)
