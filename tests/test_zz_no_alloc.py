@@ -97,3 +97,55 @@ def test_noalloc_compare_and_limit():
     sdc.sdc_fingerprint_tensor_noalloc(t, o2)
     torch.cuda.synchronize()
     assert torch.equal(o2, out)
+
+
+def test_noalloc_under_graph_capture():
+    # the callers it is for: two calls (a tensor-wide split with a compare, and a
+    # smaller tensor) captured into a graph, replayed with eager work and a
+    # data change in between; every replay equals the eager scans and the oracle
+    import workloads as W
+    lib = _abi()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(79)
+    big = torch.empty(40_000_003, dtype=torch.float32, device=DEV).normal_(0, 1, generator=g)
+    small = torch.empty(777_777, dtype=torch.float32, device=DEV).normal_(0, 1, generator=g)
+    small = small.to(torch.bfloat16)
+    ref = sdc.sdc_fingerprint_tensor(big).clone()
+    out = torch.empty((2, 4), dtype=torch.int64, device=DEV)
+    mis = torch.zeros(1, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+
+    def work():
+        mis.zero_()
+        assert _noalloc(lib, big, sdc.F32, out[0], ref=ref, mismatch=mis) == 0
+        assert _noalloc(lib, small, sdc.BF16, out[1]) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("case noalloc graph capture")
+    with torch.cuda.graph(graph):
+        work()
+    torch.cuda.synchronize()
+    expect = oracle_rows([big, small])
+    for rep in range(4):
+        if rep == 2:   # a flip in the big tensor: the compare must report it
+            W.flip_bit(big, 123_457, 5)
+            expect = oracle_rows([big, small])
+        out.fill_(-1)
+        torch.cuda.synchronize()
+        say(f"case noalloc graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = sdc.rows_numpy(out).copy()
+        torch.randn(1 << 20, device=DEV).sum().item()   # eager work between replays
+        eager = np.concatenate([sdc.rows_numpy(sdc.sdc_fingerprint_tensor(big)),
+                                sdc.rows_numpy(sdc.sdc_fingerprint_tensor(small))])
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager)
+        assert_rows_equal(got, expect)
+        assert int(mis.item()) == (1 if rep >= 2 else 0)
