@@ -309,7 +309,8 @@ int32_t sdc_fingerprint_tensor(const sdc_tensor* h_tensor, uint64_t item_bytes, 
  * one stream are safe (each call's items write their slots before its merge
  * reads them, so the array needs no clearing).  ASYNCHRONOUS on stream, like
  * sdc_fingerprint_tensor.  Errors as sdc_fingerprint_tensor, with
- * SDC_ERR_RANGE for a tensor beyond the limit. */
+ * SDC_ERR_RANGE for a tensor beyond the limit or a current device index of 64
+ * or more (the library keeps the array's address for devices 0..63). */
 int32_t sdc_fingerprint_tensor_noalloc(const sdc_tensor* h_tensor, uint64_t item_bytes,
                                        const sdc_row* d_ref, uint32_t col_mask, sdc_row* d_out,
                                        uint32_t* d_mismatch, sdc_stream_t stream);
