@@ -26,7 +26,7 @@ A segment that was not recomputed is reported in `result()["not_recomputed"]`.
 """
 import torch
 
-from . import (COL_ALL, rows_numpy, sdc_fingerprint_diff, sdc_fingerprint_tensor,
+from . import (COL_ALL, _current_stream_handle, rows_numpy, sdc_fingerprint_diff, sdc_fingerprint_tensor,
                sdc_tensor_ws_bytes)
 
 
@@ -46,17 +46,30 @@ class RecomputeAudit:
         self.original = torch.zeros((n_segments * outputs, 4), dtype=torch.int64, device=dev)
         self.recomputed = torch.zeros_like(self.original)
         self.mismatch = torch.zeros(n_segments, dtype=torch.int32, device=dev)
+        # one-row views made once: slicing a view costs about a microsecond,
+        # a sixth of a call's host time
+        self._original_rows = self.original.split(1)
+        self._recomputed_rows = self.recomputed.split(1)
+        self._mismatch_at = self.mismatch.split(1)
         self.calls = [0] * n_segments
         self._ws = {}  # one scan workspace per stream: calls on a stream run in order
 
     def _workspace(self, t):
-        st = torch.cuda.current_stream(t.device)
-        need = sdc_tensor_ws_bytes(t)
-        ws = self._ws.get(st.cuda_stream)
-        if ws is None or ws.numel() < need:
-            ws = torch.empty(max(need, 1 << 16), dtype=torch.uint8, device=t.device)
-            self._ws[st.cuda_stream] = ws
-        return ws
+        # The size is asked for only when t is larger than every tensor the
+        # stream's workspace has served: a workspace of at least 64 KiB holds
+        # the partial rows of any tensor below the tensor-wide split, and
+        # above it the need grows with the size.  (Were one too small, the
+        # scan would take a workspace of its own for that call.)
+        key = _current_stream_handle(t.device)
+        nbytes = t.numel() * t.element_size()
+        entry = self._ws.get(key)
+        if entry is None or nbytes > entry[1]:
+            need = sdc_tensor_ws_bytes(t)
+            ws = entry[0] if entry is not None else None
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(max(need, 1 << 16), dtype=torch.uint8, device=t.device)
+            entry = self._ws[key] = (ws, max(nbytes, entry[1] if entry is not None else 0))
+        return entry[0]
 
     def begin_step(self):
         """Start a step: clears the counters (a fill kernel on the current stream)."""
@@ -89,10 +102,10 @@ class RecomputeAudit:
             t = o.detach()
             r = k * self.outputs + j
             if c == 0:
-                sdc_fingerprint_tensor(t, out=self.original[r:r + 1], ws=self._workspace(t))
+                sdc_fingerprint_tensor(t, out=self._original_rows[r], ws=self._workspace(t))
             else:
-                sdc_fingerprint_tensor(t, out=self.recomputed[r:r + 1], ref=self.original[r:r + 1],
-                                       mismatch=self.mismatch[k:k + 1], col_mask=self.col_mask,
+                sdc_fingerprint_tensor(t, out=self._recomputed_rows[r], ref=self._original_rows[r],
+                                       mismatch=self._mismatch_at[k], col_mask=self.col_mask,
                                        ws=self._workspace(t))
         self.calls[k] = c + 1
 

@@ -219,6 +219,25 @@ def test_tensor_ws_bound_covers_every_cu_count(desc):
     assert 32 * worst <= ws <= 32 * max(worst, -(-nbytes // (4 << 20)) + 257)
 
 
+def test_tensor_ws_small_below_the_wide_split_and_growing_above():
+    # what the recompute audit's workspace cache relies on: with the automatic
+    # split, 64 KiB holds the partial rows of any tensor below 128 MiB, and
+    # above it the bound never falls as the tensor grows
+    sizes = {s for k in range(1, 28) for s in (1 << k, (1 << k) + 7, 3 << (k - 1))}
+    sizes |= {(m << 20) + d for m in range(127, 4097, 61) for d in (-8, 0, 8)}
+    for dtype, es in ESZ.items():
+        for align in (0, es):
+            prev = 0
+            for nbytes in sorted(sizes):
+                rc, ws = tensor_ws_bytes((0x100000 + (align if es > 1 else 0), nbytes // es, dtype, 0))
+                assert rc == 0
+                if nbytes // es * es < 128 << 20:
+                    assert ws <= 1 << 16, (dtype, nbytes)
+                else:
+                    assert ws >= prev, (dtype, nbytes)
+                    prev = ws
+
+
 def test_tensor_split_explicit_item_size_ignores_cus():
     for cus in (1, 32, 256):
         assert tensor_split((0x10002, 3 << 20, 1, 0), 65536, cus) == (0, 96, 65536)

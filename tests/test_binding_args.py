@@ -23,15 +23,19 @@ def host(*shape, dtype=torch.int64):
     return torch.zeros(shape, dtype=dtype)
 
 
-def test_arg_helper_rules():
+def test_arg_helper_rules(monkeypatch):
     t = host(8)
     with pytest.raises(ValueError, match="must be on"):
         sdc._arg(t, "x", torch.int64, 1, CUDA0)
     with pytest.raises(TypeError):
         sdc._arg([0, 1], "x", torch.int64, 1, CUDA0)
-    assert sdc._same_device(torch.device("cuda"), CUDA0)
-    assert not sdc._same_device(torch.device("cuda", 1), CUDA0)
-    assert not sdc._same_device(torch.device("cpu"), CUDA0)
+    assert not sdc._on_device(t, CUDA0)
+    assert not sdc._on_device(t, torch.device("cuda"))
+    # a tensor on GPU 1: matches "cuda" and cuda:1, not cuda:0
+    monkeypatch.setattr(torch.Tensor, "get_device", lambda self: 1)
+    assert sdc._on_device(t, torch.device("cuda"))
+    assert sdc._on_device(t, torch.device("cuda", 1))
+    assert not sdc._on_device(t, CUDA0)
 
 
 def test_plan_scans_reject_host_outputs():
@@ -67,8 +71,7 @@ def test_read_sum_and_tensor_scan_reject_host_tensors():
 
 def test_shapes_and_types_are_checked(monkeypatch):
     # pretend the host tensors are on cuda:0 so that the later checks are reached
-    monkeypatch.setattr(sdc, "_same_device", lambda a, b: True)
-    monkeypatch.setattr(torch.Tensor, "is_cuda", property(lambda self: True))
+    monkeypatch.setattr(sdc, "_on_device", lambda t, device: True)
     plan = fake_plan(3)
     with pytest.raises(ValueError, match="at least 12"):
         sdc.sdc_fingerprint_plan(plan, out=host(2, 4))
