@@ -307,7 +307,11 @@ int32_t sdc_fingerprint_tensor(const sdc_tensor* h_tensor, uint64_t item_bytes, 
  * the array: calls that overlap in time on one GPU (on different streams or
  * from different host threads) race and give wrong rows; calls in order on
  * one stream are safe (each call's items write their slots before its merge
- * reads them, so the array needs no clearing).  ASYNCHRONOUS on stream, like
+ * reads them, so the array needs no clearing).  The first call on each device
+ * looks up the array's device address (hipGetSymbolAddress, a runtime call
+ * that is not stream work): a caller that captures graphs makes one call on
+ * each device before capturing -- one on an empty tensor (numel 0, which
+ * writes the zero row) is enough.  ASYNCHRONOUS on stream, like
  * sdc_fingerprint_tensor.  Errors as sdc_fingerprint_tensor, with
  * SDC_ERR_RANGE for a tensor beyond the limit or a current device index of 64
  * or more (the library keeps the array's address for devices 0..63). */
