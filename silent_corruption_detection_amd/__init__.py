@@ -485,7 +485,9 @@ def sdc_fingerprint_tensor_noalloc(t, out, ref=None, mismatch=None, col_mask=COL
     partial rows in a static device array (at most 8192 work items, so
     tensors of up to about 31 GiB with the automatic split).  `out` (a device
     int64 row, e.g. a row of a table) and a contiguous `t` keep this call
-    free of device allocations; calls that overlap in time on one GPU race."""
+    free of device allocations; calls that overlap in time on one GPU race.
+    The first call on a device looks up the array's address: make one (an
+    empty tensor will do) before capturing a graph on that device."""
     desc, dev, keep = _one_descriptor(t, signed)
     if dev is None:
         dev = _cuda_device(None)
