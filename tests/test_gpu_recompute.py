@@ -109,6 +109,52 @@ def test_tensor_empty_missing_and_large():
     del t, plan
 
 
+def test_tensor_caller_workspace_too_small_or_empty():
+    # a caller workspace smaller than the tensor's split needs, or an empty
+    # one, is replaced for that call (the library refuses it before queuing
+    # anything); the row and the compare are those of a right-sized one
+    g = gen(17)
+    t = torch.empty(5_000_003, dtype=torch.float32, device=DEV).normal_(0, 1, generator=g)
+    ref = oracle_rows([t])
+    need = sdc.sdc_tensor_ws_bytes(t)
+    assert need > 64
+    good = torch.tensor(ref.view(np.int64), device=DEV)
+    mis = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for nb in (0, 32, need - 32, need):
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        say(f"case tensor caller workspace of {nb} bytes (needs {need})")
+        out = torch.full((1, 4), -1, dtype=torch.int64, device=DEV)
+        sdc.sdc_fingerprint_tensor(t, out=out, ws=ws)
+        assert_rows_equal(sdc.rows_numpy(out), ref)
+        sdc.sdc_fingerprint_tensor(t, out=out, ref=good, mismatch=mis, ws=ws)
+        torch.cuda.synchronize()
+        assert mis.item() == 0
+    with pytest.raises(ValueError):  # a workspace on the host is refused, not replaced
+        sdc.sdc_fingerprint_tensor(t, ws=torch.empty(need, dtype=torch.uint8))
+
+
+def test_audit_workspace_across_the_wide_split():
+    # the audit asks for a workspace size only when a larger tensor comes:
+    # outputs that grow past 128 MiB and shrink again all give the oracle's rows
+    g = gen(19)
+    sizes = [1_000_003, (128 << 20) // 4 + 5, 7_777_777, (300 << 20) // 4 + 1, (128 << 20) // 4 - 9]
+    ts = [torch.empty(n, dtype=torch.float32, device=DEV).normal_(0, 1, generator=g) for n in sizes]
+    audit = RecomputeAudit(len(ts), device=DEV)
+    audit.begin_step()
+    for k, t in enumerate(ts):
+        say(f"case audit workspace segment {k} numel={t.numel()}")
+        audit.record(k, t)
+    for k, t in enumerate(ts):   # the recomputation: same tensors
+        audit.record(k, t)
+    res = audit.result()
+    assert res["mismatched"] == [] and res["not_recomputed"] == []
+    orig, again = audit.rows()
+    ref = oracle_rows(ts)
+    assert_rows_equal(orig, ref)
+    assert_rows_equal(again, ref)
+    del ts
+
+
 def test_tensor_compare_counts_and_masks():
     g = gen(9)
     t = torch.empty(300_001, dtype=torch.float32, device=DEV).normal_(0, 1, generator=g)
