@@ -202,16 +202,22 @@ __device__ __forceinline__ uint64_t widen(uint64_t raw) {
   return raw;
 }
 
-// Head/tail element j (index within the item) at p.
+// Head/tail element j (index within the item) with raw pattern `raw`.  A zero
+// pattern adds nothing to any column (zero is never NaN/Inf).
 template <class Ty>
-__device__ __forceinline__ void scan_scalar(const unsigned char* p, uint32_t j, const NfRule& rule,
-                                            Lane& ln) {
-  const uint64_t raw = load_elem<Ty::ES>(p);
+__device__ __forceinline__ void add_scalar(uint64_t raw, uint32_t j, const NfRule& rule, Lane& ln) {
   const uint64_t v = widen<Ty::ES, Ty::SIGNED>(raw);
   ln.s += v;
   ln.w += (uint64_t)(j + 1u) * v;
   ln.x ^= raw;
   if constexpr (Ty::CHK != kChkNone) ln.nf += nf_exact(raw, rule);
+}
+
+// Head/tail element j (index within the item) at p.
+template <class Ty>
+__device__ __forceinline__ void scan_scalar(const unsigned char* p, uint32_t j, const NfRule& rule,
+                                            Lane& ln) {
+  add_scalar<Ty>(load_elem<Ty::ES>(p), j, rule, ln);
 }
 
 // xor of raw words -> xor of the elements' widened patterns.
@@ -293,38 +299,60 @@ __device__ __forceinline__ void part_reduce(Lane& ln) {
   }
 }
 
+// Sixteen zero bytes in device memory, read by wave-item lanes that have
+// nothing of their item to load.
+static __device__ __align__(16) u32x4 g_zero16;
+
 template <class Ty, uint32_t LANES>
 __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane& ln) {
   typedef Acc<Ty::ES, Ty::SIGNED, Ty::CHK> A_t;
   constexpr uint32_t es = Ty::ES;
   constexpr uint32_t E = kVecBytes / es;
+  // The head and the tail hold fewer than E elements each: at most kHT per lane.
+  constexpr uint32_t kHT = (E - 1u + LANES - 1u) / LANES;
   const Span sp = span_of<es>(it);
   const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
-  for_head_tail<LANES>(sp, l, [&](uint32_t j) {
-    scan_scalar<Ty>(sp.base + (uint64_t)j * es, j, rule, ln);
-  });
-  if (sp.nvec) {
-    const unsigned char* body = sp.base + (uint64_t)sp.h * es;
-    u32x4 v[kWaveVecs];
+  // Every load of the lane is issued before any value is used, with no
+  // branch: a lane with no head/tail element or body vector to read loads
+  // the zero vector instead (zero adds nothing to any column), so the item
+  // costs one memory latency after its descriptor.
+  const unsigned char* zero = reinterpret_cast<const unsigned char*>(&g_zero16);
+  typedef std::conditional_t<(es == 8), uint64_t, uint32_t> raw_t;
+  raw_t head[kHT], tail[kHT];
 #pragma unroll
-    for (uint32_t u = 0; u < kWaveVecs; ++u) {
-      const uint32_t vi = u * LANES + l;
-      v[u] = (vi < sp.nvec) ? load16_nt(body + (uint64_t)vi * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
-    }
-    A_t acc(rule);
+  for (uint32_t k = 0; k < kHT; ++k) {
+    const uint32_t j = k * LANES + l;
+    head[k] = (raw_t)load_elem<es>(j < sp.h ? sp.base + (uint64_t)j * es : zero);
+    tail[k] = (raw_t)load_elem<es>(j < sp.ntail ? sp.base + (uint64_t)(sp.tail0 + j) * es : zero);
+  }
+  const unsigned char* body = sp.base + (uint64_t)sp.h * es;
+  u32x4 v[kWaveVecs];
 #pragma unroll
-    for (uint32_t u = 0; u < kWaveVecs; ++u) acc.add(v[u]);
-    const uint64_t T = kWaveVecs;
-    const uint64_t A = acc.sum();
-    ln.s += A;
-    ln.w += (uint64_t)(sp.h + 1u + E * l) * A + (uint64_t)(LANES * E) * (T * A - acc.q) + acc.csum();
-    ln.x ^= acc.x;
-    if (acc.chk.flagged()) {  // rare: reload this lane's (at most 8) vectors and count exactly
-      uint32_t c = 0;
-      for (uint32_t vi = l; vi < sp.nvec; vi += LANES)
-        c += nf_vec<es>(load16_nt(body + (uint64_t)vi * kVecBytes), rule);
-      ln.nf += c;
-    }
+  for (uint32_t u = 0; u < kWaveVecs; ++u) {
+    const uint32_t vi = u * LANES + l;
+    v[u] = load16_nt(vi < sp.nvec ? body + (uint64_t)vi * kVecBytes : zero);
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < kHT; ++k) {
+    const uint32_t j = k * LANES + l;
+    add_scalar<Ty>(head[k], j, rule, ln);
+    add_scalar<Ty>(tail[k], sp.tail0 + j, rule, ln);
+  }
+  // No branch on the body's size here either (a branch would let the
+  // compiler sink the loads into it): zero vectors add nothing.
+  A_t acc(rule);
+#pragma unroll
+  for (uint32_t u = 0; u < kWaveVecs; ++u) acc.add(v[u]);
+  const uint64_t T = kWaveVecs;
+  const uint64_t A = acc.sum();
+  ln.s += A;
+  ln.w += (uint64_t)(sp.h + 1u + E * l) * A + (uint64_t)(LANES * E) * (T * A - acc.q) + acc.csum();
+  ln.x ^= acc.x;
+  if (acc.chk.flagged()) {  // rare: count this lane's vectors exactly (zero vectors count none)
+    uint32_t c = 0;
+#pragma unroll
+    for (uint32_t u = 0; u < kWaveVecs; ++u) c += acc.chk.exact(v[u]);
+    ln.nf += c;
   }
   part_reduce<LANES>(ln);
   ln.x = finish_xor<Ty>(ln.x);

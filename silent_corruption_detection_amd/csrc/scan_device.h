@@ -373,13 +373,18 @@ __device__ __forceinline__ void count_flagged_round(C& chk, const u32x4 (&v)[U],
   }
 }
 
+// Per-lane loads go through global-address-space pointers (every pointer
+// here is device memory): global loads wait on the vector-memory counter
+// alone, where flat loads of a generic pointer also hold the scalar one.
+#define SDC_GLOBAL __attribute__((address_space(1)))
+
 // Raw pattern of the ES-byte element at p.
 template <uint32_t ES>
 __device__ __forceinline__ uint64_t load_elem(const unsigned char* p) {
-  if constexpr (ES == 1) return *p;
-  if constexpr (ES == 2) return *reinterpret_cast<const unsigned short*>(p);
-  if constexpr (ES == 4) return *reinterpret_cast<const uint32_t*>(p);
-  return *reinterpret_cast<const uint64_t*>(p);
+  if constexpr (ES == 1) return *(const SDC_GLOBAL unsigned char*)p;
+  if constexpr (ES == 2) return *(const SDC_GLOBAL unsigned short*)p;
+  if constexpr (ES == 4) return *(const SDC_GLOBAL uint32_t*)p;
+  return *(const SDC_GLOBAL uint64_t*)p;
 }
 
 // Item of workgroup b among the n workgroup items of a launch on a device
@@ -433,8 +438,11 @@ inline WaveLaunch wave_launch(const uint64_t* n_wave) {
 template <uint32_t C, class F>
 __device__ __forceinline__ void run_wave_class(const WaveLaunch& w, F& f) {
   constexpr uint32_t kLanes = class_lanes(C);
-  const uint32_t j = ((blockIdx.x - w.group[C]) * kWaves + (threadIdx.x >> 6)) * (1u << C) +
-                     ((threadIdx.x & 63u) / kLanes);
+  uint32_t j = ((blockIdx.x - w.group[C]) * kWaves + (threadIdx.x >> 6)) * (1u << C) +
+               ((threadIdx.x & 63u) / kLanes);
+  // one item per wave: the index is wave-uniform, so its descriptor can come
+  // through scalar loads and the item's base address through scalar registers
+  if constexpr (kLanes == 64) j = __builtin_amdgcn_readfirstlane(j);
   if (j < w.count[C])
     f(w.first[C] + j, threadIdx.x & (kLanes - 1u), std::integral_constant<uint32_t, kLanes>());
 }
@@ -453,7 +461,7 @@ __device__ __forceinline__ void for_wave_item(const WaveLaunch& w, F&& f) {
 // Non-temporal 16-byte load through a per-lane address (the two halves of a
 // wave read different tensors, so their base addresses are not uniform).
 __device__ __forceinline__ u32x4 load16_nt(const unsigned char* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load((const SDC_GLOBAL u32x4*)p);
 }
 
 // Head, aligned body and tail of an item of ES-byte elements.
