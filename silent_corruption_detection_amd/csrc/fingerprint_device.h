@@ -299,50 +299,25 @@ __device__ __forceinline__ void part_reduce(Lane& ln) {
   }
 }
 
-// Sixteen zero bytes in device memory, read by wave-item lanes that have
-// nothing of their item to load.
-static __device__ __align__(16) u32x4 g_zero16;
-
 template <class Ty, uint32_t LANES>
 __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane& ln) {
   typedef Acc<Ty::ES, Ty::SIGNED, Ty::CHK> A_t;
   constexpr uint32_t es = Ty::ES;
   constexpr uint32_t E = kVecBytes / es;
-  // The head and the tail hold fewer than E elements each: at most kHT per lane.
-  constexpr uint32_t kHT = (E - 1u + LANES - 1u) / LANES;
   const Span sp = span_of<es>(it);
   const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
-  // Every load of the lane is issued before any value is used, with no
-  // branch: a lane with no head/tail element or body vector to read loads
-  // the zero vector instead (zero adds nothing to any column), so the item
-  // costs one memory latency after its descriptor.
-  const unsigned char* zero = reinterpret_cast<const unsigned char*>(&g_zero16);
-  typedef std::conditional_t<(es == 8), uint64_t, uint32_t> raw_t;
-  raw_t head[kHT], tail[kHT];
+  const WaveItemLoads<es, LANES> ld(sp, l);
 #pragma unroll
-  for (uint32_t k = 0; k < kHT; ++k) {
+  for (uint32_t k = 0; k < ld.kHT; ++k) {
     const uint32_t j = k * LANES + l;
-    head[k] = (raw_t)load_elem<es>(j < sp.h ? sp.base + (uint64_t)j * es : zero);
-    tail[k] = (raw_t)load_elem<es>(j < sp.ntail ? sp.base + (uint64_t)(sp.tail0 + j) * es : zero);
+    add_scalar<Ty>(ld.head[k], j, rule, ln);
+    add_scalar<Ty>(ld.tail[k], sp.tail0 + j, rule, ln);
   }
-  const unsigned char* body = sp.base + (uint64_t)sp.h * es;
-  u32x4 v[kWaveVecs];
-#pragma unroll
-  for (uint32_t u = 0; u < kWaveVecs; ++u) {
-    const uint32_t vi = u * LANES + l;
-    v[u] = load16_nt(vi < sp.nvec ? body + (uint64_t)vi * kVecBytes : zero);
-  }
-#pragma unroll
-  for (uint32_t k = 0; k < kHT; ++k) {
-    const uint32_t j = k * LANES + l;
-    add_scalar<Ty>(head[k], j, rule, ln);
-    add_scalar<Ty>(tail[k], sp.tail0 + j, rule, ln);
-  }
-  // No branch on the body's size here either (a branch would let the
-  // compiler sink the loads into it): zero vectors add nothing.
+  // No branch on the body's size (the compiler would sink the loads into
+  // it): zero vectors add nothing.
   A_t acc(rule);
 #pragma unroll
-  for (uint32_t u = 0; u < kWaveVecs; ++u) acc.add(v[u]);
+  for (uint32_t u = 0; u < kWaveVecs; ++u) acc.add(ld.v[u]);
   const uint64_t T = kWaveVecs;
   const uint64_t A = acc.sum();
   ln.s += A;
@@ -351,7 +326,7 @@ __device__ __forceinline__ void scan_small(const PlanItem& it, uint32_t l, Lane&
   if (acc.chk.flagged()) {  // rare: count this lane's vectors exactly (zero vectors count none)
     uint32_t c = 0;
 #pragma unroll
-    for (uint32_t u = 0; u < kWaveVecs; ++u) c += acc.chk.exact(v[u]);
+    for (uint32_t u = 0; u < kWaveVecs; ++u) c += acc.chk.exact(ld.v[u]);
     ln.nf += c;
   }
   part_reduce<LANES>(ln);

@@ -73,14 +73,16 @@ __device__ __forceinline__ uint32_t nonfinite_small(const PlanItem& it, uint32_t
   if constexpr (Ty::CHK != kChkNone) {
     const Span sp = span_of<es>(it);
     const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
-    for_head_tail<LANES>(sp, l, [&](uint32_t j) {
-      c += nf_exact(load_elem<es>(sp.base + (uint64_t)j * es), rule);
-    });
-    const unsigned char* body = sp.base + (uint64_t)sp.h * es;
+    const WaveItemLoads<es, LANES> ld(sp, l);  // zero where the lane has nothing: never NaN/Inf
 #pragma unroll
-    for (uint32_t u = 0; u < kWaveVecs; ++u) {
-      const uint32_t vi = u * LANES + l;
-      if (vi < sp.nvec) c += nf_vec<es>(load16_nt(body + (uint64_t)vi * kVecBytes), rule);
+    for (uint32_t k = 0; k < ld.kHT; ++k) c += nf_exact(ld.head[k], rule) + nf_exact(ld.tail[k], rule);
+    // the fast flag over the body vectors, and the exact count only if it is set
+    Chk<Ty::CHK> chk(rule);
+#pragma unroll
+    for (uint32_t u = 0; u < kWaveVecs; ++u) chk.add(ld.v[u]);
+    if (chk.flagged()) {
+#pragma unroll
+      for (uint32_t u = 0; u < kWaveVecs; ++u) c += chk.exact(ld.v[u]);
     }
   }
 #pragma unroll

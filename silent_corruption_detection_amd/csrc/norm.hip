@@ -153,17 +153,17 @@ template <class Dt, uint32_t LANES>
 __device__ __forceinline__ double sq_small(const PlanItem& it, uint32_t l) {
   constexpr uint32_t DT = Dt::DTYPE, es = dt_size<DT>();
   const Span sp = span_of<es>(it);
+  // zero where the lane has nothing: fma(0, 0, acc) is acc exactly
+  const WaveItemLoads<es, LANES> ld(sp, l);
   double acc = 0.0;
-  for_head_tail<LANES>(sp, l, [&](uint32_t j) {
-    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)j * es));
-    acc = __builtin_fma(y, y, acc);
-  });
-  const unsigned char* body = sp.base + (uint64_t)sp.h * es;
 #pragma unroll
-  for (uint32_t u = 0; u < kWaveVecs; ++u) {
-    const uint32_t vi = u * LANES + l;
-    if (vi < sp.nvec) acc = sq_vec<DT>(load16_nt(body + (uint64_t)vi * kVecBytes), acc);
+  for (uint32_t k = 0; k < ld.kHT; ++k) {
+    const double y = value_of<DT>(ld.head[k]), z = value_of<DT>(ld.tail[k]);
+    acc = __builtin_fma(y, y, acc);
+    acc = __builtin_fma(z, z, acc);
   }
+#pragma unroll
+  for (uint32_t u = 0; u < kWaveVecs; ++u) acc = sq_vec<DT>(ld.v[u], acc);
 #pragma unroll
   for (uint32_t off = LANES / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   return acc;

@@ -483,6 +483,41 @@ __device__ __forceinline__ Span span_of(const PlanItem& it) {
   return sp;
 }
 
+// Sixteen zero bytes in device memory, read by wave-item lanes that have
+// nothing of their item to load at a place.
+static __device__ __align__(16) u32x4 g_zero16;
+
+// Every load of a wave-item lane, issued before any value is used and with
+// no branch, so an item costs one memory latency after its descriptor: the
+// lane's elements of the head and of the tail (each has fewer than E = 16/ES
+// elements: element k*LANES + l of each, for k < kHT) and its kWaveVecs body
+// vectors (vector LANES*u + l).  Where the lane has nothing to read it loads
+// the zero vector instead, which adds nothing to a fingerprint, a NaN/Inf
+// count or a squared norm.  Patterns of up to 4 bytes stay 32-bit: a
+// widening right after a load would make the wave wait for it there.
+template <uint32_t ES, uint32_t LANES>
+struct WaveItemLoads {
+  static constexpr uint32_t kHT = (kVecBytes / ES - 1u + LANES - 1u) / LANES;
+  typedef std::conditional_t<(ES == 8), uint64_t, uint32_t> raw_t;
+  raw_t head[kHT], tail[kHT];
+  u32x4 v[kWaveVecs];
+  __device__ __forceinline__ WaveItemLoads(const Span& sp, uint32_t l) {
+    const unsigned char* zero = reinterpret_cast<const unsigned char*>(&g_zero16);
+#pragma unroll
+    for (uint32_t k = 0; k < kHT; ++k) {
+      const uint32_t j = k * LANES + l;
+      head[k] = (raw_t)load_elem<ES>(j < sp.h ? sp.base + (uint64_t)j * ES : zero);
+      tail[k] = (raw_t)load_elem<ES>(j < sp.ntail ? sp.base + (uint64_t)(sp.tail0 + j) * ES : zero);
+    }
+    const unsigned char* body = sp.base + (uint64_t)sp.h * ES;
+#pragma unroll
+    for (uint32_t u = 0; u < kWaveVecs; ++u) {
+      const uint32_t vi = u * LANES + l;
+      v[u] = load16_nt(vi < sp.nvec ? body + (uint64_t)vi * kVecBytes : zero);
+    }
+  }
+};
+
 // Head and tail elements of a wave item (fewer than 16 each), given out to
 // the LANES lanes of its group: f(j) with j the element's index in the item.
 template <uint32_t LANES, class F>
