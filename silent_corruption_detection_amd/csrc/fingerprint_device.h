@@ -272,12 +272,10 @@ __device__ __forceinline__ void scan_item(const PlanItem& it, Lane& ln) {
   const Span sp = span_of<es>(it);
   const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
   const uint32_t t = threadIdx.x;
-  if (t < sp.h) scan_scalar<Ty>(sp.base + (uint64_t)t * es, t, rule, ln);
-  if (t >= 128u && t - 128u < sp.ntail) {
-    const uint32_t j = sp.tail0 + (t - 128u);
-    scan_scalar<Ty>(sp.base + (uint64_t)j * es, j, rule, ln);
-  }
+  const ItemEnds<es> ends(sp, t);
   if (sp.nvec) scan_body<Ty, Cfg>(sp.base + (uint64_t)sp.h * es, sp.nvec, sp.h, rule, ln);
+  add_scalar<Ty>(ends.head, t, rule, ln);
+  add_scalar<Ty>(ends.tail, ends.tail_index(sp, t), rule, ln);
   block_reduce(ln);
   ln.x = finish_xor<Ty>(ln.x);
 }

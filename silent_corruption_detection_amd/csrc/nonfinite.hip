@@ -20,15 +20,14 @@ __device__ __forceinline__ uint32_t nonfinite_item(const PlanItem& it) {
   if constexpr (Ty::CHK != kChkNone) {  // raw integers are never NaN/Inf: nothing to read
     const Span sp = span_of<es>(it);
     const NfRule rule = nf_rule(it.dtype_flags & kItemDtypeMask);
-    if (t < sp.h) c += nf_exact(load_elem<es>(sp.base + (uint64_t)t * es), rule);
-    if (t >= 128u && t - 128u < sp.ntail)
-      c += nf_exact(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + t - 128u) * es), rule);
+    const ItemEnds<es> ends(sp, t);  // zero where the thread has none: never NaN/Inf
     if (sp.nvec) {
       const unsigned char* body = sp.base + (uint64_t)sp.h * es;
       Chk<Ty::CHK> chk(rule);
       stream_body<U, PIPE>(body, sp.nvec, [&](u32x4 v) { chk.add(v); },
                            [&](const u32x4 (&v)[U]) { count_flagged_round(chk, v, c); });
     }
+    c += nf_exact(ends.head, rule) + nf_exact(ends.tail, rule);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);

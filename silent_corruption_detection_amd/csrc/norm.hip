@@ -9,8 +9,10 @@ namespace {
 
 // ---- squared norm (the norm-based check) --------------------------------------------
 // Element values decoded exactly (every format here converts to double without
-// rounding), squared and summed in double in a fixed order: per lane in index
-// order, then fixed shuffle / LDS trees, partial slots in slot order, and one
+// rounding), squared and summed in double in a fixed order: per lane, a
+// workgroup item's body vectors in index order and then its head and tail
+// element, a wave item's head and tail elements and then its body vectors;
+// then fixed shuffle / LDS trees, partial slots in slot order, and one
 // workgroup for the total -- so a plan gives the same bits on every run.
 template <uint32_t DT>
 struct DtTag {
@@ -118,20 +120,16 @@ __device__ __forceinline__ double sq_item(const PlanItem& it) {
   constexpr uint32_t DT = Dt::DTYPE, es = dt_size<DT>();
   const Span sp = span_of<es>(it);
   const uint32_t t = threadIdx.x;
+  const ItemEnds<es> ends(sp, t);  // zero where the thread has none: fma(0, 0, acc) is acc
   double acc = 0.0;
-  if (t < sp.h) {
-    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)t * es));
-    acc = y * y;
-  }
-  if (t >= 128u && t - 128u < sp.ntail) {
-    const double y = value_of<DT>(load_elem<es>(sp.base + (uint64_t)(sp.tail0 + t - 128u) * es));
-    acc = __builtin_fma(y, y, acc);
-  }
   // lane t adds its vectors t, t + 256, t + 512, ... in that order, whatever
-  // the round depth and pipelining
+  // the round depth and pipelining, then its head and its tail element
   if (sp.nvec)
     stream_body<U, PIPE>(sp.base + (uint64_t)sp.h * es, sp.nvec,
                          [&](u32x4 v) { acc = sq_vec<DT>(v, acc); });
+  const double y = value_of<DT>(ends.head), z = value_of<DT>(ends.tail);
+  acc = __builtin_fma(y, y, acc);
+  acc = __builtin_fma(z, z, acc);
   return acc;
 }
 

@@ -518,6 +518,27 @@ struct WaveItemLoads {
   }
 };
 
+// The head element t and the tail element t - 128 of a workgroup item's
+// thread t (heads and tails have fewer than 16 elements), loaded with no
+// branch before the item's body loads are issued and used after them, so an
+// item's start costs one memory latency instead of three: a thread with no
+// such element loads the zero vector, which adds nothing.
+template <uint32_t ES>
+struct ItemEnds {
+  typedef std::conditional_t<(ES == 8), uint64_t, uint32_t> raw_t;
+  raw_t head, tail;
+  __device__ __forceinline__ ItemEnds(const Span& sp, uint32_t t) {
+    const unsigned char* zero = reinterpret_cast<const unsigned char*>(&g_zero16);
+    const uint32_t k = t - 128u;  // wraps for t < 128: no tail element there
+    head = (raw_t)load_elem<ES>(t < sp.h ? sp.base + (uint64_t)t * ES : zero);
+    tail = (raw_t)load_elem<ES>(k < sp.ntail ? sp.base + (uint64_t)(sp.tail0 + k) * ES : zero);
+  }
+  // index in the item of the tail element (any value where tail is zero)
+  __device__ __forceinline__ static uint32_t tail_index(const Span& sp, uint32_t t) {
+    return sp.tail0 + (t - 128u);
+  }
+};
+
 // Head and tail elements of a wave item (fewer than 16 each), given out to
 // the LANES lanes of its group: f(j) with j the element's index in the item.
 template <uint32_t LANES, class F>
