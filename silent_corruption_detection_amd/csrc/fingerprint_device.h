@@ -153,7 +153,7 @@ struct BodyCfg {
   static constexpr int U = U_;
   static constexpr bool PIPE = PIPE_;
 };
-typedef BodyCfg<4, true> DefaultBody;  // ~106 VGPRs: 4 workgroups per CU
+typedef BodyCfg<4, true> DefaultBody;  // ~104 VGPRs: 4 workgroups per CU
 typedef BodyCfg<8, true> DeepBody;     // ~188 VGPRs: deeper pipeline, 2 workgroups per CU
 typedef BodyCfg<kWideU, false> WideBody;  // the wide shape: one workgroup per CU
 // Plans whose items average at least this many bytes use DeepBody (measured:
@@ -211,13 +211,6 @@ __device__ __forceinline__ void add_scalar(uint64_t raw, uint32_t j, const NfRul
   ln.w += (uint64_t)(j + 1u) * v;
   ln.x ^= raw;
   if constexpr (Ty::CHK != kChkNone) ln.nf += nf_exact(raw, rule);
-}
-
-// Head/tail element j (index within the item) at p.
-template <class Ty>
-__device__ __forceinline__ void scan_scalar(const unsigned char* p, uint32_t j, const NfRule& rule,
-                                            Lane& ln) {
-  add_scalar<Ty>(load_elem<Ty::ES>(p), j, rule, ln);
 }
 
 // xor of raw words -> xor of the elements' widened patterns.
@@ -284,7 +277,7 @@ __device__ __forceinline__ void scan_item(const PlanItem& it, Lane& ln) {
 // The aligned body has at most LANES x kWaveVecs vectors; lane l loads vectors
 // LANES*u + l for u = 0 .. kWaveVecs-1 all at once (T = kWaveVecs, missing
 // vectors count as zero), then W_lane = (h+1+E*l)*A + LANES*E*(T*A - Q) + C.
-// Loads go through per-lane addresses: the two halves of a wave may read
+// Loads go through per-lane addresses: the groups of a wave (up to 8) read
 // different tensors.
 template <uint32_t LANES>
 __device__ __forceinline__ void part_reduce(Lane& ln) {

@@ -539,18 +539,5 @@ struct ItemEnds {
   }
 };
 
-// Head and tail elements of a wave item (fewer than 16 each), given out to
-// the LANES lanes of its group: f(j) with j the element's index in the item.
-template <uint32_t LANES, class F>
-__device__ __forceinline__ void for_head_tail(const Span& sp, uint32_t l, F&& f) {
-  if constexpr (LANES >= 32) {  // head on the first lanes, tail on the upper half
-    if (l < sp.h) f(l);
-    if (l >= LANES / 2 && l - LANES / 2 < sp.ntail) f(sp.tail0 + (l - LANES / 2));
-  } else {
-    for (uint32_t j = l; j < sp.h; j += LANES) f(j);
-    for (uint32_t j = l; j < sp.ntail; j += LANES) f(sp.tail0 + j);
-  }
-}
-
 }  // namespace
 }  // namespace sdc
