@@ -11,8 +11,10 @@
 // second launch merges them (a single shared atomic per workgroup instead
 // costs about 15 % of the rate: every workgroup's update of one address is
 // serialised across the XCDs).  Its rate is the streaming-read bandwidth the
-// chip reaches with that load structure, the ceiling against which the scans'
-// bandwidth is read.
+// chip reaches with that load structure over one buffer of random words: a
+// reference the scans' bandwidth is read against, not an upper bound (the
+// list scan over a model's parameters has measured up to 1.2 % above it in
+// the same run).
 #include "scan_device.h"
 
 namespace sdc {
